@@ -81,6 +81,9 @@ def _load():
     lib.oracle_mmq_q4k_points.argtypes = [_u8p, _i64, _i64, _u8p, _i64,
                                           _i64p, _i64p, _i64, _f64p]
     lib.oracle_mmq_q4k_points.restype = None
+    lib.oracle_mmq_q6k_from_plane.argtypes = [_i8p, _i64, _i64, _i64, _u8p, _i64, _i64, _i64,
+                                              _u8p, _i64, _f64p]
+    lib.oracle_mmq_q6k_from_plane.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -217,6 +220,16 @@ def mmq_q4k_points(W, od, id_, q8, nt, tt, jj) -> np.ndarray:
     out = np.zeros(len(tt), dtype=np.float64)
     _load().oracle_mmq_q4k_points(_u8(W), od, id_, _u8(q8), nt, tt, jj, len(tt), out)
     return out
+
+
+def mmq_q6k_from_plane(plane, row_stride, sb_stride, W, bstride, od, id_, q8, nt) -> np.ndarray:
+    """q6_K GEMM reading the quants from a dense plane at the given strides
+    (scales and d from W); see the C function for the mutant it models."""
+    plane = np.ascontiguousarray(plane, dtype=np.int8).reshape(-1)
+    y = np.zeros((nt, od), dtype=np.float64)
+    _load().oracle_mmq_q6k_from_plane(plane, plane.size, row_stride, sb_stride, _u8(W), bstride,
+                                      od, id_, _u8(q8), nt, y.reshape(-1))
+    return y
 
 
 def num_threads() -> int:

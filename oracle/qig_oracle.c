@@ -518,6 +518,49 @@ void oracle_mmq_q4k_points(const uint8_t *W, int64_t od, int64_t id, const uint8
     mmq_q4k_impl(W, od, id, q8, nt, tt, jj, n, out);
 }
 
+/*
+ * q6_K GEMM whose quants are read from a dense centred plane at the given
+ * strides: element e of super-block sb of row j is plane[j*row_stride +
+ * sb*sb_stride + e] (reads past plane_bytes count as 0); d and the scales
+ * still come from the raw blocks.  With the dense plane's own strides (id,
+ * 256) this is oracle_mmq_q6k; with the padded raw-W strides (nsb*bstride,
+ * bstride) it reproduces the consumer mistake analysed on the r44 page
+ * ("W_exp stride mismatch root cause", s2.3), which the tests use as a
+ * mutant that parity must reject.
+ */
+void oracle_mmq_q6k_from_plane(const int8_t *plane, int64_t plane_bytes, int64_t row_stride,
+                               int64_t sb_stride, const uint8_t *W, int64_t bstride, int64_t od,
+                               int64_t id, const uint8_t *q8, int64_t nt, double *y)
+{
+    const int64_t nsb = id / 256, nb32 = id / 32;
+    int8_t *qa = malloc((size_t)nt * id);
+    double *da = malloc(sizeof(double) * (size_t)nt * nb32);
+    double *ss = malloc(sizeof(double) * (size_t)nt * nb32);
+    q8_plane(q8, nt, id, qa, da, ss);
+    #pragma omp parallel for schedule(dynamic)
+    for (int64_t j = 0; j < od; ++j) {
+        int8_t *c6 = malloc((size_t)id);
+        int8_t *sc = malloc((size_t)(16 * nsb));
+        double *d = malloc(sizeof(double) * (size_t)nsb);
+        q6k_row(W, bstride, id, j, c6, sc, d);          /* scales and d from W */
+        for (int64_t sb = 0; sb < nsb; ++sb)
+            for (int e = 0; e < 256; ++e) {
+                int64_t off = j * row_stride + sb * sb_stride + e;
+                c6[256 * sb + e] = (off >= 0 && off < plane_bytes) ? plane[off] : 0;
+            }
+        for (int64_t t = 0; t < nt; ++t) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < 16 * nsb; ++s) {
+                int64_t p = idot(qa + t * id + 16 * s, c6 + 16 * s, 16);
+                acc += da[t * nb32 + s / 2] * d[s / 16] * (double)sc[s] * (double)p;
+            }
+            y[t * od + j] = acc;
+        }
+        free(c6); free(sc); free(d);
+    }
+    free(qa); free(da); free(ss);
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

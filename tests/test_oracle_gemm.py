@@ -225,3 +225,24 @@ def test_tolerance_helper():
     assert ok and w == 0.0
     ok, _ = oracle.within_tolerance(np.array([1.01, 2.0]), np.array([1.0, 2.0]))
     assert not ok
+
+
+def test_dense_plane_consumer_and_stride_mutant(oracle_mod):
+    """Consumer gate on the CPU (r44 page 'W_exp stride mismatch root cause',
+    s2.3-2.5): the dense plane read at its own strides (id, 256) gives the
+    raw-block result exactly; read at the padded raw-W strides (nsb*224, 224)
+    it gives a wrong result that the parity tolerance rejects, although every
+    byte of the plane is correct."""
+    g = inputs.rng(28)
+    nt, od, id_ = 6, 9, 768
+    W = inputs.q6k_weights(g, od, id_)
+    x = g.standard_normal((nt, id_), dtype=np.float32)
+    q8 = oracle_mod.quantize_q8_pad40(x)
+    plane = oracle_mod.expand_q6k_dense(W, 224, od, id_)
+    y_raw = oracle_mod.mmq_q6k(W, 224, od, id_, q8, nt)
+    y_ok = oracle_mod.mmq_q6k_from_plane(plane, id_, 256, W, 224, od, id_, q8, nt)
+    assert np.array_equal(y_ok, y_raw)
+    nsb = id_ // 256
+    y_bad = oracle_mod.mmq_q6k_from_plane(plane, nsb * 224, 224, W, 224, od, id_, q8, nt)
+    ok, worst = oracle_mod.within_tolerance(y_bad, y_raw)
+    assert not ok and worst > 10
