@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the k-quant prefill MMQ hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input at
+the q-projection shape (od = id = 3584, nt = 512):
+    quantize_q8_pad40(x4) -> mmq_q4k(W4)            (q4_K GEMM)
+    quantize_q8_pad40(x6) -> mmq_q6k(W6)            (q6_K GEMM, raw blocks)
+                          -> mmq_q6k(W6, W_exp)     (q6_K GEMM, dense-plane arm)
+Inputs are resident in HBM before timing; the dense plane is built once
+beforehand (it is registration-time work) and timed separately.
+
+Prints one JSON line: value = int8 TOPS of the whole step (3 GEMMs x
+2*nt*od*id ops / step time), the per-kernel average durations from HIP
+events recorded on the launch stream, a roofline entry for the dominant
+kernel and the CPU oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MMQ int8 TOPS + µs/GEMM, q4_K & q6_K 3584×3584×nt512; % of int8 MFMA peak"
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+NT, OD, ID = 512, 3584, 3584
+SEED4, SEED6 = 20261, 20262   # seed base + workload index
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(W4, x4, W6, x6):
+    """The oracle as it stands, on the host cores: the full step's arithmetic
+    (both quantizations and the three GEMMs), repeated until ~10 s."""
+    import oracle
+    ops = 3 * 2.0 * NT * OD * ID
+    reps, total = 0, 0.0
+    while total < 10.0 and reps < 20:
+        t0 = time.perf_counter()
+        q84 = oracle.quantize_q8_pad40(x4)
+        oracle.mmq_q4k(W4, OD, ID, q84, NT)
+        q86 = oracle.quantize_q8_pad40(x6)
+        oracle.mmq_q6k(W6, 224, OD, ID, q86, NT)
+        plane = oracle.expand_q6k_dense(W6, 224, OD, ID)
+        oracle.mmq_q6k_from_plane(plane, ID, 256, W6, 224, OD, ID, q86, NT)
+        total += time.perf_counter() - t0
+        reps += 1
+    return {
+        "value": round(ops * reps / total / 1e12, 4),
+        "unit": "TOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"the full step (2 quantizations, q4_K + q6_K raw + q6_K dense-plane GEMMs, "
+                  f"nt={NT}, od=id={ID}) repeated {reps}x in {total:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quant_integer_gemm_amd as qig
+    from quant_integer_gemm_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    qig.load()
+    dev = torch.device("cuda:0")
+    g4 = inputs.WORKLOADS[1][0]
+    g6 = inputs.WORKLOADS[2][0]
+    W4, x4 = inputs.make_gemm_inputs(g4, SEED4)
+    W6, x6 = inputs.make_gemm_inputs(g6, SEED6)
+    W4d = torch.from_numpy(W4).to(dev)
+    W6d = torch.from_numpy(W6).to(dev)
+    x4d = torch.from_numpy(x4).to(dev)
+    x6d = torch.from_numpy(x6).to(dev)
+    nb = qig.q8_pad40_bytes(NT, ID)
+    q84 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    q86 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    y4 = torch.empty((NT, OD), dtype=torch.float32, device=dev)
+    y6 = torch.empty((NT, OD), dtype=torch.float32, device=dev)
+    y6e = torch.empty((NT, OD), dtype=torch.float32, device=dev)
+    wexp = torch.empty((OD, ID), dtype=torch.int8, device=dev)
+
+    # registration-time expansion, timed on its own
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(3):
+        qig.expand_q6k_dense(W6d, 224, OD, ID, out=wexp)
+    ev[0].record()
+    for _ in range(10):
+        qig.expand_q6k_dense(W6d, 224, OD, ID, out=wexp)
+    ev[1].record()
+    torch.cuda.synchronize()
+    expand_us = ev[0].elapsed_time(ev[1]) * 1e3 / 10
+
+    names = ["quantize_x4", "mmq_q4k", "quantize_x6", "mmq_q6k_raw", "mmq_q6k_wexp"]
+    calls = [
+        lambda: qig.quantize_q8_pad40(x4d, out=q84),
+        lambda: qig.mmq_q4k(W4d, OD, ID, q84, NT, y=y4, ldy=OD),
+        lambda: qig.quantize_q8_pad40(x6d, out=q86),
+        lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, y=y6, ldy=OD),
+        lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, W_exp=wexp, y=y6e, ldy=OD),
+    ]
+
+    def step(events=None):
+        for k, fn in enumerate(calls):
+            if events is not None:
+                events[k][0].record()
+            fn()
+            if events is not None:
+                events[k][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel HIP events on the launch stream
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in calls] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([evs[s][k][0].elapsed_time(evs[s][k][1]) for s in range(args.steps)])) * 1e3
+           for k, n in enumerate(names)}
+    # step time without the event overhead: a second pass without per-kernel events
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_plain = time.perf_counter() - t0
+    ms_per_step = wall_plain / args.steps * 1e3
+
+    gemm_ops = 2.0 * NT * OD * ID
+    value = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
+    gemms = ["mmq_q4k", "mmq_q6k_raw", "mmq_q6k_wexp"]
+    dom = max(gemms, key=lambda n: per[n])
+    achieved = gemm_ops / (per[dom] * 1e-6) / 1e12
+    # algorithmic bytes per launch of each GEMM: raw weights + pad40 plane + fp32 y, once each
+    wbytes = {"mmq_q4k": OD * (ID // 256) * 144, "mmq_q6k_raw": OD * (ID // 256) * 224,
+              "mmq_q6k_wexp": OD * ID + OD * (ID // 256) * 224}
+    abytes = nb + NT * OD * 4
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "q4_K + q6_K GEMMs od=id=3584, nt=512 (quantize, mmq_q4k, mmq_q6k raw, "
+                        "mmq_q6k dense-plane arm)",
+            "nt": NT, "od": OD, "id": ID, "seeds": [SEED4, SEED6],
+        },
+        "per_kernel_us": {k: round(v, 3) for k, v in per.items()},
+        "per_gemm_tops": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12, 1) for n in gemms},
+        "per_gemm_pct_int8_peak": {n: round(100 * gemm_ops / (per[n] * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2)
+                                   for n in gemms},
+        "per_gemm_hbm_gbs": {n: round((wbytes[n] + abytes) / (per[n] * 1e-6) / 1e9, 1) for n in gemms},
+        "expand_q6k_dense_us": round(expand_us, 3),
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W4, x4, W6, x6)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * qig.h -- C ABI of libqig.so, the MI355X (gfx950) k-quant prefill MMQ.
+ *
+ * The operation (the "minfer CUDA optimization steps" pages, r20/r21/r43/r44):
+ * weights stored as 256-element k-quant super-blocks (q6_K or q4_K) times
+ * activations quantized per token into q8 "pad40" blocks, contracted as
+ * int8 x int8 -> int32 sub-block dot products and rescaled to an fp32
+ * output y[nt][od] = x[nt][id] . W[od][id]^T.
+ *
+ * Conventions shared by every entry point
+ *  - All buffer pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises inside a call; work is enqueued on
+ *    `stream` (0 = the null stream) and the call returns at once.
+ *  - Shapes are element counts.  nt (tokens) and od (weight rows) may be 0:
+ *    the call then does nothing and returns QIG_OK.  id (the contraction
+ *    length) must be a positive multiple of 256 for the GEMMs (one super-
+ *    block) and of 32 for the quantizer (one pad40 chunk).
+ *  - Return value: QIG_OK, or a negative QIG_E* code; nothing is enqueued
+ *    when an argument check fails.  qig_strerror() names a code.
+ *  - Outputs never alias inputs.  NaN/Inf inputs give unspecified output.
+ *  - Calls on one stream run in order; calls on different streams that write
+ *    the same buffer race.
+ */
+#ifndef QIG_H
+#define QIG_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QIG_OK 0
+#define QIG_EINVAL (-1)   /* bad shape, stride or size */
+#define QIG_EALIGN (-2)   /* pointer or leading dimension misaligned */
+#define QIG_ELAUNCH (-3)  /* the HIP runtime reported a launch error */
+
+/* Size in bytes of a pad40 plane for nt tokens of id elements:
+ * nt * (id / 32) * 40.  Returns 0 for invalid arguments. */
+size_t q8_pad40_bytes(int64_t nt, int64_t id);
+
+/* Human-readable name of a return code (static string, never NULL). */
+const char *qig_strerror(int code);
+
+/*
+ * quantize_q8_pad40 -- per-token activation quantization into pad40 blocks.
+ * Layout (r21 page "Coalesced block-linear A staging", s2.1; r20 page
+ * "Split-phase A staging", s3.2): one 40-byte block per (token t, chunk c of
+ * 32 elements) at byte offset (t * id/32 + c) * 40, holding fp16 d at bytes
+ * 0-1, zero at 2-3, 32 int8 quants at 4-35 and fp32 ssum at 36-39.
+ * Fill rule: d32 = max|x| / 127 (fp32 division), q = round-half-away(x / d32)
+ * clamped to [-127, 127] (all 0 when d32 == 0), d = fp16 of d32 (round to
+ * nearest even, subnormals kept), ssum = d * sum(q) in fp32 (exact).
+ *
+ *   x      [nt][ldx] fp32, 16-byte aligned, ldx >= id, ldx % 4 == 0
+ *   q8     q8_pad40_bytes(nt, id) bytes, 16-byte aligned; every byte written
+ * Errors: QIG_EINVAL (nt < 0, id <= 0 or id % 32, ldx < id),
+ *         QIG_EALIGN (x or q8 not 16-byte aligned, ldx % 4).
+ */
+int quantize_q8_pad40(const float *x, int64_t nt, int64_t id, int64_t ldx,
+                      void *q8, hipStream_t stream);
+
+/*
+ * mmq_q4k -- y[nt][od] = pad40(x) . W^T for q4_K weights.
+ * W is [od][id/256] blocks of 144 bytes, contiguous: fp16 d at 0, fp16 dmin
+ * at 2, twelve bytes of packed 6-bit (scale, min) pairs at 4, 128 bytes of
+ * 4-bit quants at 16 (GGUF block_q4_K; the pages name the format but do not
+ * print its layout).  Per 32-element sub-block b of super-block sb:
+ *   y += da(t,c) * d * sc_b * P4(t,j,c) - dmin * m_b * ssum(t,c),
+ *   P4 = int32 sum over the chunk of q8 quants times 4-bit quants,
+ * c = 8*sb + b being the matching pad40 chunk.
+ *
+ *   W      16-byte aligned
+ *   q8     pad40 plane of nt tokens x id, 16-byte aligned
+ *   y      [nt][ldy] fp32, ldy >= od; overwritten (not accumulated),
+ *          4-byte aligned
+ * Errors: QIG_EINVAL (nt < 0, od < 0, id <= 0 or id % 256, ldy < od),
+ *         QIG_EALIGN, QIG_ELAUNCH.
+ */
+int mmq_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt,
+            float *y, int64_t ldy, hipStream_t stream);
+
+/*
+ * mmq_q6k -- y[nt][od] = pad40(x) . W^T for q6_K weights.
+ * W is the padded raw plane (r44 page "W_exp stride mismatch root cause",
+ * s2.2): row j, super-block sb at W + j*nsb*bstride + sb*bstride, nsb =
+ * id/256; each block holds ql[128] at 0, qh[64] at 128, 16 int8 sub-block
+ * scales at 192 and fp16 d at 208; bytes 210..bstride-1 are ignored.
+ * Sixteen 16-element sub-blocks, each with its own d*sc (r44 page s1.1):
+ *   y += da(t, 8*sb + s/2) * d * sc_s * P6(t,j,sb,s).
+ * Element map of the 6-bit quants: r44 page s3.2 (centred value in
+ * [-32, 31]).
+ *
+ *   bstride  >= 210 and a multiple of 16 (224 for the padded in-VRAM form)
+ *   W_exp    NULL: quants are decoded from W.  Non-NULL: the dense centred
+ *            plane made by expand_q6k_dense (od x id int8, row stride id,
+ *            super-block stride 256, 16-byte aligned) supplies the quants;
+ *            d and the scales are still read from W.  Both arms give
+ *            bit-identical y.
+ *   W, q8, y as for mmq_q4k.
+ * Errors: QIG_EINVAL (shapes as mmq_q4k, bad bstride), QIG_EALIGN,
+ *         QIG_ELAUNCH.
+ */
+int mmq_q6k(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od,
+            int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
+            hipStream_t stream);
+
+/*
+ * expand_q6k_dense -- registration-time expansion of raw q6_K into the dense
+ * centred-int8 plane W_exp (r43 page "PC-sampling attribution", s3.2; r44
+ * page s2.2 and s3.2): W_exp[j*id + 256*sb + e] = centred element e of
+ * super-block sb of row j.
+ *
+ *   W      padded raw plane as for mmq_q6k, 16-byte aligned
+ *   W_exp  od * id bytes, 16-byte aligned; every byte written
+ * Errors: QIG_EINVAL (od < 0, id <= 0 or id % 256, bad bstride),
+ *         QIG_EALIGN, QIG_ELAUNCH.
+ */
+int expand_q6k_dense(const void *W, int64_t bstride, int64_t od, int64_t id,
+                     int8_t *W_exp, hipStream_t stream);
+
+/*
+ * Test exports: the int32 sub-block partials of the same kernels, for the
+ * window of tokens [t0, t1) and rows [j0, j1), written to
+ * P[(t - t0)][(j - j0)][sub] (int32, 4-byte aligned), where sub runs over all
+ * 8*nsb q4_K sub-blocks of 32 (P4) or 16*nsb q6_K sub-blocks of 16 (P6).
+ * Same argument rules as the GEMMs plus 0 <= t0 <= t1 <= nt and
+ * 0 <= j0 <= j1 <= od (QIG_EINVAL otherwise).
+ */
+int mmq_q4k_partials(const void *W, int64_t od, int64_t id, const void *q8,
+                     int64_t nt, int64_t t0, int64_t t1, int64_t j0, int64_t j1,
+                     int32_t *P, hipStream_t stream);
+int mmq_q6k_partials(const void *W, int64_t bstride, const int8_t *W_exp,
+                     int64_t od, int64_t id, const void *q8, int64_t nt,
+                     int64_t t0, int64_t t1, int64_t j0, int64_t j1, int32_t *P,
+                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QIG_H */

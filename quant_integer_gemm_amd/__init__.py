@@ -1,1 +1,19 @@
-"""k-quant prefill MMQ for MI355X (gfx950): Python binding of the C-ABI library."""
+"""k-quant prefill MMQ for MI355X (gfx950).
+
+q4_K / q6_K super-block weights times per-token q8 "pad40" activations,
+int8 x int8 -> int32 sub-block dot products on the int8 MFMA, rescaled to
+fp32 in a fused epilogue.  The compute is in libqig.so (hand-written HIP,
+C ABI declared in include/qig.h); this package is its thin ctypes binding.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    QigError,
+    expand_q6k_dense,
+    load,
+    mmq_q4k,
+    mmq_q4k_partials,
+    mmq_q6k,
+    mmq_q6k_partials,
+    q8_pad40_bytes,
+    quantize_q8_pad40,
+)

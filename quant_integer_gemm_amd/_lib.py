@@ -1,0 +1,151 @@
+"""ctypes binding of libqig.so: argument marshalling only.
+
+Every step of the MMQ runs in the HIP kernels of libqig.so; this module only
+turns torch device tensors into raw pointers, picks the current HIP stream and
+raises on a non-zero return code.  There is no CPU fallback: if the library is
+missing or the tensors are not on the GPU, the call fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libqig.so")
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+# name -> (restype, argtypes), mirroring include/qig.h
+SIGNATURES = {
+    "q8_pad40_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "qig_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "quantize_q8_pad40": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "mmq_q4k": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "mmq_q6k": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "expand_q6k_dense": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "mmq_q4k_partials": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
+    "mmq_q6k_partials": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+                                        _vp, _vp]),
+}
+
+
+class QigError(RuntimeError):
+    pass
+
+
+def load(path: str | None = None):
+    """Load libqig.so (once) and attach the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise QigError(f"{p} is not built: run `python -m quant_integer_gemm_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load().qig_strerror(rc).decode()
+        raise QigError(f"{what} failed: {msg} (code {rc})")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise QigError(f"{name} must be a GPU tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def q8_pad40_bytes(nt: int, id_: int) -> int:
+    return int(load().q8_pad40_bytes(nt, id_))
+
+
+def quantize_q8_pad40(x, id_: int | None = None, out=None, stream=None):
+    """fp32 x[nt][ldx] (GPU) -> uint8 pad40 plane of q8_pad40_bytes(nt, id) bytes."""
+    import torch
+    if x.dim() != 2 or x.dtype != torch.float32 or x.stride(1) != 1:
+        raise QigError("x must be a 2-D fp32 tensor with unit column stride")
+    nt, _ = x.shape
+    id_ = x.shape[1] if id_ is None else id_
+    ldx = x.stride(0) if nt > 1 else max(x.shape[1], id_)
+    nbytes = q8_pad40_bytes(nt, id_)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _check(load().quantize_q8_pad40(_dev_ptr(x, "x"), nt, id_, ldx, _dev_ptr(out, "q8"), _stream(stream)),
+           "quantize_q8_pad40")
+    return out
+
+
+def _out_y(y, nt, od, ldy, device):
+    import torch
+    if y is None:
+        y = torch.empty((nt, od), dtype=torch.float32, device=device)
+        ldy = od
+    elif ldy is None:
+        ldy = y.stride(0) if y.dim() == 2 else od
+    return y, ldy
+
+
+def mmq_q4k(W, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, stream=None):
+    """y[nt][od] = pad40 activations x q4_K weights^T (fp32, overwritten)."""
+    y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _check(load().mmq_q4k(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
+                          _stream(stream)), "mmq_q4k")
+    return y
+
+
+def mmq_q6k(W, bstride: int, od: int, id_: int, q8, nt: int, W_exp=None, y=None, ldy: int | None = None,
+            stream=None):
+    """y[nt][od] = pad40 activations x q6_K weights^T; W_exp (dense plane) optional."""
+    y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _check(load().mmq_q6k(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_,
+                          _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy, _stream(stream)), "mmq_q6k")
+    return y
+
+
+def expand_q6k_dense(W, bstride: int, od: int, id_: int, out=None, stream=None):
+    """Raw q6_K plane -> dense centred int8 W_exp[od][id]."""
+    import torch
+    if out is None:
+        out = torch.empty((od, id_), dtype=torch.int8, device=W.device)
+    _check(load().expand_q6k_dense(_dev_ptr(W, "W"), bstride, od, id_, _dev_ptr(out, "W_exp"),
+                                   _stream(stream)), "expand_q6k_dense")
+    return out
+
+
+def mmq_q4k_partials(W, od, id_, q8, nt, t0, t1, j0, j1, stream=None):
+    """int32 P4[t1-t0][j1-j0][8*nsb] from the q4_K kernel (test export)."""
+    import torch
+    P = torch.empty((t1 - t0, j1 - j0, 8 * (id_ // 256)), dtype=torch.int32, device=W.device)
+    _check(load().mmq_q4k_partials(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8, "q8"), nt, t0, t1, j0, j1,
+                                   _dev_ptr(P, "P"), _stream(stream)), "mmq_q4k_partials")
+    return P
+
+
+def mmq_q6k_partials(W, bstride, od, id_, q8, nt, t0, t1, j0, j1, W_exp=None, stream=None):
+    """int32 P6[t1-t0][j1-j0][16*nsb] from the q6_K kernel (test export)."""
+    import torch
+    P = torch.empty((t1 - t0, j1 - j0, 16 * (id_ // 256)), dtype=torch.int32, device=W.device)
+    _check(load().mmq_q6k_partials(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_,
+                                   _dev_ptr(q8, "q8"), nt, t0, t1, j0, j1, _dev_ptr(P, "P"),
+                                   _stream(stream)), "mmq_q6k_partials")
+    return P

@@ -1,0 +1,116 @@
+// abi.hip -- the C ABI of libqig.so: argument checks, then one launch on the
+// caller's stream.  Declarations and the full contract are in include/qig.h.
+#include <qig.h>
+
+#include "qig_launch.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int rc_from_launch(int r) { return r == 0 ? QIG_OK : (r == -1 ? QIG_EINVAL : QIG_ELAUNCH); }
+
+int check_gemm(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, const void *out,
+               int64_t ldy)
+{
+    if (nt < 0 || od < 0 || id <= 0 || id % 256 != 0) return QIG_EINVAL;
+    if (ldy < od) return QIG_EINVAL;
+    if (nt == 0 || od == 0) return QIG_OK;
+    if (!W || !q8 || !out) return QIG_EINVAL;
+    if (!aligned(W, 16) || !aligned(q8, 16) || !aligned(out, 4)) return QIG_EALIGN;
+    return QIG_OK;
+}
+
+bool bad_bstride(int64_t bstride) { return bstride < 210 || bstride % 16 != 0; }
+
+bool bad_window(int64_t nt, int64_t od, int64_t t0, int64_t t1, int64_t j0, int64_t j1)
+{
+    return t0 < 0 || t1 < t0 || t1 > nt || j0 < 0 || j1 < j0 || j1 > od;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q8_pad40_bytes(int64_t nt, int64_t id)
+{
+    if (nt < 0 || id <= 0 || id % 32 != 0) return 0;
+    return (size_t)nt * (size_t)(id / 32) * 40u;
+}
+
+const char *qig_strerror(int code)
+{
+    switch (code) {
+    case QIG_OK: return "ok";
+    case QIG_EINVAL: return "invalid shape, stride or size";
+    case QIG_EALIGN: return "pointer or leading dimension misaligned";
+    case QIG_ELAUNCH: return "HIP launch error";
+    default: return "unknown error";
+    }
+}
+
+int quantize_q8_pad40(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q8, hipStream_t stream)
+{
+    if (nt < 0 || id <= 0 || id % 32 != 0 || ldx < id) return QIG_EINVAL;
+    if (nt == 0) return QIG_OK;
+    if (!x || !q8) return QIG_EINVAL;
+    if (!aligned(x, 16) || !aligned(q8, 16) || ldx % 4 != 0) return QIG_EALIGN;
+    return rc_from_launch(qig::launch_quantize(x, nt, id, ldx, q8, stream));
+}
+
+int mmq_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
+            hipStream_t stream)
+{
+    int rc = check_gemm(W, od, id, q8, nt, y, ldy);
+    if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    qig::MmqLaunch L = {4, W, nullptr, q8, y, nullptr, 144, od, id, nt, ldy, 0, nt, 0, od};
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
+int mmq_q6k(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id, const void *q8,
+            int64_t nt, float *y, int64_t ldy, hipStream_t stream)
+{
+    if (bad_bstride(bstride)) return QIG_EINVAL;
+    int rc = check_gemm(W, od, id, q8, nt, y, ldy);
+    if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    if (W_exp && !aligned(W_exp, 16)) return QIG_EALIGN;
+    qig::MmqLaunch L = {6, W, W_exp, q8, y, nullptr, bstride, od, id, nt, ldy, 0, nt, 0, od};
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
+int expand_q6k_dense(const void *W, int64_t bstride, int64_t od, int64_t id, int8_t *W_exp,
+                     hipStream_t stream)
+{
+    if (bad_bstride(bstride) || od < 0 || id <= 0 || id % 256 != 0) return QIG_EINVAL;
+    if (od == 0) return QIG_OK;
+    if (!W || !W_exp) return QIG_EINVAL;
+    if (!aligned(W, 16) || !aligned(W_exp, 16)) return QIG_EALIGN;
+    return rc_from_launch(qig::launch_expand_q6k(W, bstride, od, id, W_exp, stream));
+}
+
+int mmq_q4k_partials(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, int64_t t0,
+                     int64_t t1, int64_t j0, int64_t j1, int32_t *P, hipStream_t stream)
+{
+    int rc = check_gemm(W, od, id, q8, nt, P, od);
+    if (rc != QIG_OK) return rc;
+    if (bad_window(nt, od, t0, t1, j0, j1)) return QIG_EINVAL;
+    if (t1 == t0 || j1 == j0) return QIG_OK;
+    qig::MmqLaunch L = {4, W, nullptr, q8, nullptr, P, 144, od, id, nt, 0, t0, t1, j0, j1};
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
+int mmq_q6k_partials(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id,
+                     const void *q8, int64_t nt, int64_t t0, int64_t t1, int64_t j0, int64_t j1, int32_t *P,
+                     hipStream_t stream)
+{
+    if (bad_bstride(bstride)) return QIG_EINVAL;
+    int rc = check_gemm(W, od, id, q8, nt, P, od);
+    if (rc != QIG_OK) return rc;
+    if (W_exp && !aligned(W_exp, 16)) return QIG_EALIGN;
+    if (bad_window(nt, od, t0, t1, j0, j1)) return QIG_EINVAL;
+    if (t1 == t0 || j1 == j0) return QIG_OK;
+    qig::MmqLaunch L = {6, W, W_exp, q8, nullptr, P, bstride, od, id, nt, 0, t0, t1, j0, j1};
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// qig_device.h -- device-side helpers shared by the gfx950 kernels of libqig.
+//
+// CDNA4 facts relied on (checked on the device by the parity tests):
+//  * v_mfma_i32_32x32x32_i8: a wave multiplies a 32x32 int8 A (rows m) by a
+//    32x32 int8 B (columns n) over K = 32.  Lane l supplies 16 bytes of row
+//    m = l % 32 of A and 16 bytes of column n = l % 32 of B; the same
+//    (lane half l / 32, byte) position of A and B meets in the sum, so loading
+//    bytes 16*(l/32) .. +15 of a 32-wide chunk into lane l makes lanes 0-31
+//    carry k = 0..15 and lanes 32-63 carry k = 16..31.
+//  * The 32x32 result: lane l, register i holds column n = l % 32 and row
+//    m = 8*(i/4) + 4*(l/32) + i%4 (the same for the f32 32x32x2 form).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qig {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Starting an int32 MFMA accumulator at the bit pattern of 1.5*2^23 makes the
+// result, read as fp32, equal 1.5*2^23 + P exactly while |P| < 2^22.  Then
+// fma(D, s, -1.5*2^23*s) == round(P*s) in one instruction whenever
+// 1.5*2^23*s is exact (s with at most 22 significant bits).
+constexpr int MAGIC_I = 0x4B400000;
+constexpr float MAGIC_F = 12582912.0f;
+
+__device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c)
+{
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Reinterpret an int32 as fp32.  Takes the value by copy: clang's
+// __builtin_bit_cast applied directly to an ext-vector element (v[i]) reads
+// element 0 whatever i is, so vector elements must pass through a scalar.
+__device__ __forceinline__ float as_float(int v)
+{
+    return __builtin_bit_cast(float, v);
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
+}
+
+// Row of the 32x32 MFMA result held by register i of a lane in half `hh`.
+__device__ __forceinline__ int mfma_row(int i, int hh)
+{
+    return 8 * (i >> 2) + 4 * hh + (i & 3);
+}
+
+// Position of token row tau (0..31) in a per-row scale vector laid out so
+// that each lane half reads its 16 rows contiguously, in register order.
+__device__ __forceinline__ int row_slot(int tau)
+{
+    return 16 * ((tau >> 2) & 1) + 4 * (tau >> 3) + (tau & 3);
+}
+
+// q6_K: four centred int8 weights from one ql dword and one qh dword.
+// quarter qq (0..3) picks the nibble (low for 0,1; high for 2,3) and the
+// 2-bit field of qh.  Bytes are in [0, 63] before centring; OR-ing 0x80 keeps
+// the per-byte subtraction of 32 from borrowing across bytes, XOR 0x80 then
+// gives the two's-complement value - 32.
+__device__ __forceinline__ uint32_t q6_centred(uint32_t qlw, uint32_t qhw, int qq)
+{
+    uint32_t nib = (qq < 2) ? (qlw & 0x0F0F0F0Fu) : ((qlw >> 4) & 0x0F0F0F0Fu);
+    uint32_t hi2 = ((qhw >> (2 * qq)) & 0x03030303u) << 4;
+    return ((nib | hi2 | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+}
+
+// q4_K 6-bit scale and min of sub-block b from the twelve packed bytes S.
+__device__ __forceinline__ void q4_scale_min(const uint8_t *S, int b, int &sc, int &m)
+{
+    if (b < 4) {
+        sc = S[b] & 63;
+        m = S[b + 4] & 63;
+    } else {
+        sc = (S[b + 4] & 15) | ((S[b - 4] >> 6) << 4);
+        m = (S[b + 4] >> 4) | ((S[b] >> 6) << 4);
+    }
+}
+
+}  // namespace qig

@@ -1,0 +1,121 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quant_integer_gemm_amd as qig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qig.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*([A-Za-z_]\w*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for n in ["quantize_q8_pad40", "mmq_q4k", "mmq_q6k", "expand_q6k_dense", "q8_pad40_bytes",
+              "qig_strerror", "mmq_q4k_partials", "mmq_q6k_partials"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qig.load()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+        assert n in qig._lib.SIGNATURES, n
+
+
+def test_sizes_and_strerror():
+    assert qig.q8_pad40_bytes(512, 3584) == 512 * 112 * 40
+    assert qig.q8_pad40_bytes(0, 256) == 0
+    assert qig.q8_pad40_bytes(3, 33) == 0
+    assert qig.q8_pad40_bytes(-1, 32) == 0
+    lib = qig.load()
+    assert lib.qig_strerror(0) == b"ok"
+    assert lib.qig_strerror(-1).startswith(b"invalid")
+    assert lib.qig_strerror(-2).startswith(b"pointer")
+    assert lib.qig_strerror(-3).startswith(b"HIP")
+    assert lib.qig_strerror(7) == b"unknown error"
+
+
+A16 = ctypes.c_void_p(0x10000)     # aligned fake device addresses, never dereferenced:
+B16 = ctypes.c_void_p(0x20000)     # every call below fails its argument check first
+MIS = ctypes.c_void_p(0x10004)
+
+
+@pytest.mark.parametrize("args,rc", [
+    ((A16, 4, 100, 100, B16, None), -1),      # id % 32
+    ((A16, -1, 64, 64, B16, None), -1),       # nt < 0
+    ((A16, 4, 64, 32, B16, None), -1),        # ldx < id
+    ((MIS, 4, 64, 64, B16, None), -2),        # x misaligned
+    ((A16, 4, 64, 66, B16, None), -2),        # ldx % 4
+    ((A16, 4, 64, 64, MIS, None), -2),        # q8 misaligned
+    ((A16, 0, 64, 64, B16, None), 0),         # empty: no-op
+])
+def test_quantize_argument_checks(args, rc):
+    assert qig.load().quantize_q8_pad40(*args) == rc
+
+
+@pytest.mark.parametrize("args,rc", [
+    ((A16, 8, 300, B16, 4, A16, 8, None), -1),     # id % 256
+    ((A16, 8, 0, B16, 4, A16, 8, None), -1),       # id == 0
+    ((A16, -8, 256, B16, 4, A16, 8, None), -1),    # od < 0
+    ((A16, 8, 256, B16, 4, A16, 7, None), -1),     # ldy < od
+    ((MIS, 8, 256, B16, 4, A16, 8, None), -2),
+    ((A16, 8, 256, MIS, 4, A16, 8, None), -2),
+    ((A16, 8, 256, B16, 4, ctypes.c_void_p(0x10002), 8, None), -2),
+    ((A16, 8, 256, B16, 0, A16, 8, None), 0),      # nt == 0
+    ((A16, 0, 256, B16, 4, A16, 0, None), 0),      # od == 0
+])
+def test_mmq_q4k_argument_checks(args, rc):
+    assert qig.load().mmq_q4k(*args) == rc
+
+
+@pytest.mark.parametrize("args,rc", [
+    ((A16, 208, None, 8, 256, B16, 4, A16, 8, None), -1),   # bstride < 210
+    ((A16, 216, None, 8, 256, B16, 4, A16, 8, None), -1),   # bstride % 16
+    ((A16, 224, MIS, 8, 256, B16, 4, A16, 8, None), -2),    # W_exp misaligned
+    ((A16, 224, None, 8, 512, B16, 0, A16, 8, None), 0),
+])
+def test_mmq_q6k_argument_checks(args, rc):
+    assert qig.load().mmq_q6k(*args) == rc
+
+
+def test_expand_and_partials_argument_checks():
+    lib = qig.load()
+    assert lib.expand_q6k_dense(A16, 224, 4, 100, B16, None) == -1
+    assert lib.expand_q6k_dense(A16, 200, 4, 256, B16, None) == -1
+    assert lib.expand_q6k_dense(MIS, 224, 4, 256, B16, None) == -2
+    assert lib.expand_q6k_dense(A16, 224, 0, 256, B16, None) == 0
+    # window outside the output
+    assert lib.mmq_q4k_partials(A16, 8, 256, B16, 4, 0, 5, 0, 8, A16, None) == -1
+    assert lib.mmq_q4k_partials(A16, 8, 256, B16, 4, 2, 1, 0, 8, A16, None) == -1
+    assert lib.mmq_q6k_partials(A16, 224, None, 8, 256, B16, 4, 0, 4, 0, 9, A16, None) == -1
+    # empty window
+    assert lib.mmq_q6k_partials(A16, 224, None, 8, 256, B16, 4, 1, 1, 0, 8, A16, None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(2, 32)
+    with pytest.raises(qig.QigError):
+        qig.quantize_q8_pad40(x)
+
+
+def test_oracle_not_imported_by_product():
+    """The product package never imports the oracle."""
+    pkg = os.path.join(ROOT, "quant_integer_gemm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "qig_oracle" not in text, f

@@ -1,0 +1,284 @@
+"""GPU parity of the HIP path against the CPU oracle (run on an MI355X).
+
+Bars: pad40 bytes, W_exp bytes and int32 sub-block partials bit-exact; fp32 y
+within |y - y_ref| <= max(1e-4 |y_ref|, 1e-3 rms(y_ref)) per element, y_ref
+being the oracle's fp64 result.  Shapes span several tiles (64 tokens x 128
+rows per workgroup) with ragged tails, the five workloads at full size (all
+outputs for the nt=512 GEMMs, sampled outputs for the nt=2630 layer), and the
+degenerate cases (empty inputs, one token, one row).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quant_integer_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def qig():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import quant_integer_gemm_amd as q
+    q.load()
+    return q
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _x_variant(g, nt, id_, kind):
+    x = g.standard_normal((nt, id_), dtype=np.float32)
+    if kind == "scaled2":
+        x *= np.float32(2.0)
+    elif kind == "tiny":                    # fp16-subnormal scales
+        x *= np.float32(1e-6)
+    elif kind == "ties":                    # integer inputs: many exact halves
+        x = np.round(x * 40).astype(np.float32)
+    elif kind == "zeros":                   # whole zero chunks
+        x[::3, : min(id_, 64)] = 0.0
+    elif kind == "heavy":
+        x = (g.standard_t(2.0, size=(nt, id_)) * 3).astype(np.float32)
+    return x
+
+
+# ---------------------------------------------------------------------------
+# quantize
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("nt,id_,kind", [
+    (16, 512, "normal"), (1, 32, "normal"), (3, 96, "ties"), (37, 4096, "tiny"),
+    (70, 1024, "zeros"), (9, 2048, "heavy"), (512, 3584, "normal"), (512, 18944, "scaled2"),
+    (2630, 18944, "normal"),
+])
+def test_quantize_bit_exact(qig, nt, id_, kind):
+    g = inputs.rng(1000 + nt + id_)
+    x = _x_variant(g, nt, id_, kind)
+    want = oracle.quantize_q8_pad40(x)
+    got = host(qig.quantize_q8_pad40(dev(x)))
+    assert got.shape == want.shape
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+
+
+def test_quantize_row_stride(qig):
+    g = inputs.rng(3)
+    x = g.standard_normal((5, 160), dtype=np.float32)
+    want = oracle.quantize_q8_pad40(x, id_=128)
+    got = host(qig.quantize_q8_pad40(dev(x), id_=128))
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# GEMM helpers
+# ---------------------------------------------------------------------------
+def _weights(qtype, g, od, id_, bstride=224):
+    if qtype == "q4_K":
+        return inputs.q4k_weights(g, od, id_)
+    return inputs.q6k_weights(g, od, id_, bstride=bstride)
+
+
+def _gpu_gemm(qig, qtype, Wd, od, id_, q8d, nt, bstride=224, Wexp=None, y=None, ldy=None):
+    if qtype == "q4_K":
+        return qig.mmq_q4k(Wd, od, id_, q8d, nt, y=y, ldy=ldy)
+    return qig.mmq_q6k(Wd, bstride, od, id_, q8d, nt, W_exp=Wexp, y=y, ldy=ldy)
+
+
+def _oracle_gemm(qtype, W, od, id_, q8, nt, bstride=224):
+    if qtype == "q4_K":
+        return oracle.mmq_q4k(W, od, id_, q8, nt)
+    return oracle.mmq_q6k(W, bstride, od, id_, q8, nt)
+
+
+def _assert_close(y, y_ref, what=""):
+    ok, worst = oracle.within_tolerance(y, y_ref)
+    assert ok, f"{what}: worst error/allowance = {worst:.3g}"
+
+
+SMALL = [(16, 256, 512), (1, 1, 256), (70, 130, 768), (129, 257, 512), (64, 128, 256),
+         (200, 300, 1024), (3, 1000, 256), (65, 129, 2304)]
+
+
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("nt,od,id_", SMALL)
+def test_gemm_small(qig, qtype, nt, od, id_):
+    g = inputs.rng(nt * 7 + od * 13 + id_)
+    W = _weights(qtype, g, od, id_)
+    x = g.standard_normal((nt, id_), dtype=np.float32)
+    q8 = oracle.quantize_q8_pad40(x)
+    y = host(_gpu_gemm(qig, qtype, dev(W), od, id_, dev(q8), nt))
+    _assert_close(y, _oracle_gemm(qtype, W, od, id_, q8, nt), f"{qtype} {nt}x{od}x{id_}")
+
+
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+def test_gemm_integer_special_case_exact(qig, qtype):
+    """Unit scales and integer activations with max |x| = 127 per chunk: the
+    fp32 output must equal the integer matmul exactly."""
+    g = inputs.rng(31)
+    nt, od, id_ = 70, 150, 512
+    x = g.integers(-127, 128, size=(nt, id_)).astype(np.float32)
+    x[:, ::32] = 127.0
+    if qtype == "q4_K":
+        W = inputs.q4k_weights(g, od, id_).reshape(od, -1, 144)
+        W[:, :, 0:2] = np.array([1.0], dtype=np.float16).view(np.uint8)
+        W[:, :, 2:4] = 0
+        W[:, :, 4:16] = np.array([1, 1, 1, 1, 0, 0, 0, 0, 1, 1, 1, 1], dtype=np.uint8)
+        W = W.reshape(od, -1)
+        wq = np.zeros((od, id_), dtype=np.int64)
+        for j in range(od):
+            for sb in range(id_ // 256):
+                q, _, _, _, _ = oracle.q4k_decode_block(W[j, sb * 144:(sb + 1) * 144])
+                wq[j, 256 * sb:256 * sb + 256] = q
+    else:
+        W = inputs.q6k_weights(g, od, id_).reshape(od, -1, 224)
+        W[:, :, 192:208] = 1
+        W[:, :, 208:210] = np.array([1.0], dtype=np.float16).view(np.uint8)
+        W = W.reshape(od, -1)
+        wq = oracle.expand_q6k_dense(W, 224, od, id_).astype(np.int64)
+    want = (x.astype(np.int64) @ wq.T).astype(np.float64)
+    assert np.max(np.abs(want)) < 2 ** 24
+    q8 = oracle.quantize_q8_pad40(x)
+    y = host(_gpu_gemm(qig, qtype, dev(W), od, id_, dev(q8), nt))
+    assert np.array_equal(y.astype(np.float64), want)
+
+
+def test_q4k_subnormal_scales(qig):
+    g = inputs.rng(32)
+    nt, od, id_ = 40, 140, 512
+    W = inputs.q4k_weights(g, od, id_).reshape(od, -1, 144)
+    W[:, :, 0:2] = np.array([3e-6], dtype=np.float16).view(np.uint8)    # subnormal d
+    W[:, :, 2:4] = np.array([5e-7], dtype=np.float16).view(np.uint8)    # subnormal dmin
+    W = W.reshape(od, -1)
+    x = g.standard_normal((nt, id_), dtype=np.float32) * np.float32(1e-6)   # subnormal da
+    q8 = oracle.quantize_q8_pad40(x)
+    y = host(qig.mmq_q4k(dev(W), od, id_, dev(q8), nt))
+    _assert_close(y, oracle.mmq_q4k(W, od, id_, q8, nt), "subnormal")
+
+
+# ---------------------------------------------------------------------------
+# partials
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("nt,od,id_,win", [
+    (16, 256, 512, None), (70, 130, 768, None), (129, 257, 512, (60, 129, 100, 257)),
+    (512, 3584, 3584, (40, 90, 3450, 3584)),
+])
+def test_partials_bit_exact(qig, qtype, nt, od, id_, win):
+    g = inputs.rng(41 + nt + od)
+    W = _weights(qtype, g, od, id_)
+    x = g.standard_normal((nt, id_), dtype=np.float32)
+    q8 = oracle.quantize_q8_pad40(x)
+    t0, t1, j0, j1 = win if win else (0, nt, 0, od)
+    if qtype == "q4_K":
+        want = oracle.q4k_partials(W, od, id_, q8, nt, t0, t1, j0, j1)
+        got = host(qig.mmq_q4k_partials(dev(W), od, id_, dev(q8), nt, t0, t1, j0, j1))
+    else:
+        want = oracle.q6k_partials(W, 224, od, id_, q8, nt, t0, t1, j0, j1)
+        got = host(qig.mmq_q6k_partials(dev(W), 224, od, id_, dev(q8), nt, t0, t1, j0, j1))
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), f"{np.sum(got != want)} partials differ"
+
+
+# ---------------------------------------------------------------------------
+# W_exp arm: content gate, then consumer gate
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("nt,od,id_,bstride", [(16, 256, 512, 224), (70, 130, 768, 240),
+                                               (512, 3584, 3584, 224)])
+def test_wexp_content_and_consumer(qig, nt, od, id_, bstride):
+    g = inputs.rng(51 + od)
+    W = inputs.q6k_weights(g, od, id_, bstride=bstride)
+    x = g.standard_normal((nt, id_), dtype=np.float32)
+    q8 = oracle.quantize_q8_pad40(x)
+    Wd, q8d = dev(W), dev(q8)
+    wexp = qig.expand_q6k_dense(Wd, bstride, od, id_)
+    want_plane = oracle.expand_q6k_dense(W, bstride, od, id_)
+    assert np.array_equal(host(wexp), want_plane)                        # content
+    y_raw = host(qig.mmq_q6k(Wd, bstride, od, id_, q8d, nt))
+    y_exp = host(qig.mmq_q6k(Wd, bstride, od, id_, q8d, nt, W_exp=wexp))
+    assert np.array_equal(y_raw.view(np.uint32), y_exp.view(np.uint32))  # consumer: identical
+    _assert_close(y_exp, oracle.mmq_q6k(W, bstride, od, id_, q8, nt), "W_exp arm")
+    t1, j1 = min(nt, 40), min(od, 140)
+    p_raw = host(qig.mmq_q6k_partials(Wd, bstride, od, id_, q8d, nt, 0, t1, 0, j1))
+    p_exp = host(qig.mmq_q6k_partials(Wd, bstride, od, id_, q8d, nt, 0, t1, 0, j1, W_exp=wexp))
+    assert np.array_equal(p_raw, p_exp)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+def _run_workload_gemm(qig, gm, seed, sample=None):
+    W, x = inputs.make_gemm_inputs(gm, seed)
+    nt, od, id_ = gm.nt, gm.od, gm.id
+    xd = dev(x)
+    q8d = qig.quantize_q8_pad40(xd)
+    q8 = oracle.quantize_q8_pad40(x)
+    assert np.array_equal(host(q8d), q8)
+    y = host(_gpu_gemm(qig, gm.qtype, dev(W), od, id_, q8d, nt))
+    if sample is None:
+        _assert_close(y, _oracle_gemm(gm.qtype, W, od, id_, q8, nt), gm.name)
+        return
+    g = inputs.rng(seed + 99)
+    tt = np.concatenate([g.integers(0, nt, sample), [0, nt - 1, nt - 1, 0]])
+    jj = np.concatenate([g.integers(0, od, sample), [0, od - 1, 0, od - 1]])
+    if gm.qtype == "q4_K":
+        ref = oracle.mmq_q4k_points(W, od, id_, q8, nt, tt, jj)
+    else:
+        ref = oracle.mmq_q6k_points(W, 224, od, id_, q8, nt, tt, jj)
+    # the rms floor comes from the full GPU output (its rms equals the reference's
+    # to far better than the tolerance, so this only sets the floor's scale)
+    rms = float(np.sqrt(np.mean(y.astype(np.float64) ** 2)))
+    ok, worst = oracle.within_tolerance(y[tt, jj], ref, rms=rms)
+    assert ok, f"{gm.name}: worst error/allowance = {worst:.3g}"
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_workload_full(qig, cfg):
+    for i, gm in enumerate(inputs.WORKLOADS[cfg]):
+        _run_workload_gemm(qig, gm, inputs.SEED_BASE + cfg + 10 * i)
+
+
+def test_workload_layer_sampled(qig):
+    for i, gm in enumerate(inputs.WORKLOADS[4]):
+        _run_workload_gemm(qig, gm, inputs.SEED_BASE + 4 + 10 * i, sample=512)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+def test_empty_and_strided_output(qig, qtype):
+    g = inputs.rng(61)
+    nt, od, id_ = 33, 70, 512
+    W = _weights(qtype, g, od, id_)
+    x = g.standard_normal((nt, id_), dtype=np.float32)
+    q8 = oracle.quantize_q8_pad40(x)
+    Wd, q8d = dev(W), dev(q8)
+    # empty: nothing written
+    y0 = torch.full((4, od), 7.0, device="cuda")
+    _gpu_gemm(qig, qtype, Wd, od, id_, q8d, 0, y=y0, ldy=od)
+    assert np.all(host(y0) == 7.0)
+    # ldy > od: padding columns untouched, NaN-filled outputs overwritten
+    ybig = torch.full((nt, od + 13), float("nan"), device="cuda")
+    _gpu_gemm(qig, qtype, Wd, od, id_, q8d, nt, y=ybig, ldy=od + 13)
+    yb = host(ybig)
+    assert np.all(np.isnan(yb[:, od:]))
+    _assert_close(yb[:, :od], _oracle_gemm(qtype, W, od, id_, q8, nt), "ldy")
+
+
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+def test_deterministic(qig, qtype):
+    g = inputs.rng(71)
+    nt, od, id_ = 300, 520, 1024
+    W = _weights(qtype, g, od, id_)
+    x = g.standard_normal((nt, id_), dtype=np.float32)
+    Wd, q8d = dev(W), qig.quantize_q8_pad40(dev(x))
+    a = host(_gpu_gemm(qig, qtype, Wd, od, id_, q8d, nt))
+    b = host(_gpu_gemm(qig, qtype, Wd, od, id_, q8d, nt))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
