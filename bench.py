@@ -40,7 +40,34 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy 3x (outside the timed region) so that "
+                        "HBM counters taken over this run can be scaled by a kernel of known traffic")
     return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """sha256 of the GEMM kernel source: HBM-traffic figures recorded from
+    counters are only reported while the kernel they were taken on is unchanged."""
+    import hashlib
+    with open(os.path.join(ROOT, "quant_integer_gemm_amd", "csrc", "mmq.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel`, from the counter summary kept under
+    profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when
+    there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "mmq_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("mmq_hip_sha256") != kernel_source_digest():
+        return None
+    v = rec.get("bytes_per_launch", {}).get(kernel)
+    return None if v is None else int(v)
 
 
 def cpu_baseline(W4, x4, W6, x6):
@@ -49,7 +76,7 @@ def cpu_baseline(W4, x4, W6, x6):
     import oracle
     ops = 3 * 2.0 * NT * OD * ID
     reps, total = 0, 0.0
-    while total < 10.0 and reps < 20:
+    while total < 12.0 and reps < 200:
         t0 = time.perf_counter()
         q84 = oracle.quantize_q8_pad40(x4)
         oracle.mmq_q4k(W4, OD, ID, q84, NT)
@@ -119,46 +146,52 @@ def main():
         lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, W_exp=wexp, y=y6e, ldy=OD),
     ]
 
-    def step(events=None):
-        for k, fn in enumerate(calls):
-            if events is not None:
-                events[k][0].record()
+    def step():
+        for fn in calls:
             fn()
-            if events is not None:
-                events[k][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    # timed region: K steps, per-kernel HIP events on the launch stream
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in calls] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {n: float(np.mean([evs[s][k][0].elapsed_time(evs[s][k][1]) for s in range(args.steps)])) * 1e3
-           for k, n in enumerate(names)}
-    # step time without the event overhead: a second pass without per-kernel events
+    # timed region: K whole steps back to back
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    wall_plain = time.perf_counter() - t0
-    ms_per_step = wall_plain / args.steps * 1e3
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # per-kernel durations: each call launched K times back to back between one
+    # pair of HIP events recorded on the launch stream (an event pair around
+    # every single launch would add the event's own latency to each figure)
+    per = {}
+    for n, fn in zip(names, calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per[n] = e0.elapsed_time(e1) * 1e3 / args.steps
 
     gemm_ops = 2.0 * NT * OD * ID
     value = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
     gemms = ["mmq_q4k", "mmq_q6k_raw", "mmq_q6k_wexp"]
     dom = max(gemms, key=lambda n: per[n])
     achieved = gemm_ops / (per[dom] * 1e-6) / 1e12
-    # algorithmic bytes per launch of each GEMM: raw weights + pad40 plane + fp32 y, once each
+    # algorithmic bytes per launch of each GEMM: weights (raw blocks; for the dense-plane arm
+    # the plane plus d and the 16 scales of each block) + pad40 plane + fp32 y, once each
     wbytes = {"mmq_q4k": OD * (ID // 256) * 144, "mmq_q6k_raw": OD * (ID // 256) * 224,
-              "mmq_q6k_wexp": OD * ID + OD * (ID // 256) * 224}
+              "mmq_q6k_wexp": OD * ID + OD * (ID // 256) * 18}
     abytes = nb + NT * OD * 4
     out = {
         "metric": METRIC,
@@ -191,7 +224,7 @@ def main():
             "peak": PEAK_INT8_TOPS,
             "unit": "TOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(dom),
         },
     }
     if not args.no_cpu_baseline:

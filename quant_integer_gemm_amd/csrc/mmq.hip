@@ -9,24 +9,33 @@
 // with int32 P over a 16- (q6_K) or 32-element (q4_K) sub-block.
 //
 // Design (MI355X-first; the pages' IMMA kernels are prior art only):
-//  * Workgroup of 256 threads = 4 waves computes a 64-token x 128-row tile;
-//    each wave a 32-token x 64-row tile = two 32x32 MFMA tiles that share the
-//    token-side per-row scales.
-//  * MFMA rows are tokens, columns are weight rows, so each lane owns one
+//  * A workgroup of 256 threads = 4 waves owns a 64-token x 64-row output
+//    tile, one 32x32 MFMA tile per wave.  Its double-buffered LDS stage is
+//    under 80 KB, so two workgroups share a CU and each SIMD runs two waves
+//    of different workgroups that do not move in lock-step.
+//  * MFMA rows are tokens and columns weight rows, so each lane owns one
 //    weight row: the per-(row, chunk) weight scale is a lane constant and the
-//    per-(token, chunk) fp16 activation scale is a per-register value read
-//    straight from LDS as fp16 (v_fma_mix consumes it without conversion).
+//    per-(token, chunk) fp16 activation scale a per-register value read from
+//    LDS as fp16 (v_fma_mix consumes it without conversion).
 //  * K advances one super-block (256) per step.  The raw blocks of step k+1
-//    are loaded into registers with 16-byte loads while step k computes, then
-//    decoded (nibble / 2-bit recombination to int8) into the other half of a
-//    double-buffered LDS stage: one barrier per super-block.
-//  * Epilogue per 32-chunk and MFMA tile: the int8 MFMA accumulates onto the
-//    1.5*2^23 bias so one fma turns the int32 partial into P*w exactly once
-//    rounded; a v_fma_mix folds in the fp16 activation scale.  2 VALU ops per
-//    output and chunk (q4_K), 4 for q6_K (two 16-element sub-blocks, each its
-//    own MFMA with the other half of K zeroed).
+//    are fetched with 16-byte loads while step k computes, then decoded
+//    (nibbles / 6-bit recombination to int8, scales to fp32) into the other
+//    half of the LDS stage: one barrier per step.
+//  * Within a step a wave runs its 8 chunks as a software pipeline: the MFMA
+//    of chunk c+1 is issued before the VALU epilogue of chunk c, chunk c+2's
+//    MFMA operands and chunk c+1's scales are fetched from LDS while it runs,
+//    and value pins keep the compiler from collapsing the pipeline.
+//  * Epilogue per 32-chunk: the int8 MFMA accumulates onto the 1.5*2^23 bias
+//    so one fma turns the int32 partial into P*w, rounded once; a v_fma_mix
+//    folds in the fp16 activation scale: 2 VALU ops per output and chunk for
+//    q4_K, 4 for q6_K (two 16-element sub-blocks, each its own MFMA with the
+//    other half of K zeroed).
 //  * q4_K min term: -dmin*m*ssum summed over chunks is a K = id/32 fp32 matrix
 //    product, done on the fp32 MFMA (32x32x2) into a second accumulator.
+//  * Workgroups are numbered so that each of the 8 XCDs (each with its own L2)
+//    gets a contiguous run of tiles: one slice of weight rows, all tokens.
+#include <utility>
+
 #include "qig_device.h"
 #include "qig_launch.h"
 
@@ -34,7 +43,7 @@ namespace qig {
 
 constexpr int NTHR = 256;
 constexpr int TT = 64;    // tokens per workgroup tile
-constexpr int TJ = 128;   // weight rows per workgroup tile
+constexpr int TJ = 64;    // weight rows per workgroup tile
 constexpr int NCH = 8;    // 32-element chunks per super-block
 
 // One super-block of staged operands.
@@ -44,7 +53,7 @@ struct Stage;
 template <>
 struct Stage<4> {
     uint8_t a[NCH][TT][32];     // activation quants (16-byte halves swizzled)
-    uint16_t ad[NCH][TT];       // activation fp16 d, row_slot order per 32 tokens
+    float ad[NCH][TT];          // activation d (fp16 value as fp32), row_slot order
     float as[NCH][TT];          // activation ssum
     uint8_t b[NCH][TJ][32];     // weight nibbles 0..15 as int8
     float bs[NCH][TJ];          // d * sc
@@ -54,14 +63,16 @@ struct Stage<4> {
 template <>
 struct Stage<6> {
     uint8_t a[NCH][TT][32];
-    uint16_t ad[NCH][TT];
+    float ad[NCH][TT];
     uint8_t b[NCH][TJ][32];     // centred int8 weights
     float bs[NCH][TJ][2];       // d * sc of the two 16-element sub-blocks
 };
 
-// 16-byte half h of row r lives at half (h ^ swz(r)) so that the 16 lanes of
-// one LDS access phase touch 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 1; }
+// The 16-byte half h of row r is stored at half h ^ swz(r).  An LDS access
+// phase serves 8 (32 banks) or 16 (64 banks) lanes reading 16 bytes of
+// consecutive rows 32 bytes apart; flipping the half on bit 2 xor bit 3 of
+// the row spreads both kinds of phase over distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 struct MmqArgs {
     const uint8_t *W;
@@ -74,203 +85,289 @@ struct MmqArgs {
     int nbt;                  // token tiles in the window
 };
 
-// ---------------------------------------------------------------------------
-// global -> register loads of one super-block, and register -> LDS decode
-// ---------------------------------------------------------------------------
-template <int QT, bool WEXP>
-struct Regs;
-
-template <>
-struct Regs<4, false> {
-    u32x4 a[5];   // two pad40 blocks of one token (80 bytes)
-    u32x4 h;      // q4_K header: d, dmin, 12 scale bytes
-    u32x4 q[4];   // 64 nibble bytes
-};
-
-template <bool WEXP>
-struct Regs6 {
-    u32x4 a[5];
-    u32x4 q[WEXP ? 8 : 6];   // W_exp: 128 centred bytes; raw: ql 64 B + qh 32 B
-    u32x4 sc;                // 16 int8 scales
-    uint32_t d;              // fp16 d in the low half
-};
-template <>
-struct Regs<6, false> : Regs6<false> {};
-template <>
-struct Regs<6, true> : Regs6<true> {};
-
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p)
 {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-// Activations: thread -> (token tau = tid/4, block pair p = tid%4).
-template <typename R>
-__device__ __forceinline__ void load_a(R &r, const MmqArgs &g, int64_t tw0, int64_t sb)
+__device__ __forceinline__ void st16(uint8_t *p, u32x4 v)
 {
-    const int tid = threadIdx.x;
-    const int tau = tid >> 2, p = tid & 3;
-    const int64_t t = tw0 + tau;
-    const int64_t nb32 = g.id / 32;
-    if (t < g.nt) {
-        const uint8_t *src = g.q8 + ((t * nb32) + 8 * sb + 2 * p) * 40;
-#pragma unroll
-        for (int k = 0; k < 5; ++k) r.a[k] = ld16(src + 16 * k);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 5; ++k) r.a[k] = u32x4{0, 0, 0, 0};
-    }
+    *reinterpret_cast<u32x4 *>(p) = v;
 }
 
-template <int QT, typename R>
-__device__ __forceinline__ void store_a(Stage<QT> &s, const R &r)
+// Ordering points for the software pipeline.  MFMAs and VALU arithmetic are
+// free-floating in the compiler's instruction DAG, which tends to hoist all
+// MFMAs of a step and sink all epilogues, keeping every result live.  An empty
+// volatile asm is ordered with the LDS operations around it; making it read
+// one value and redefine another pins "this MFMA is issued before that
+// epilogue starts" and "this epilogue is done before the next loads".
+template <typename T>
+__device__ __forceinline__ void pin(T &x) { asm volatile("" : "+v"(x)); }
+template <typename T, typename U>
+__device__ __forceinline__ void pin_after(T &x, const U &y) { asm volatile("" : "+v"(x) : "v"(y)); }
+
+// ---------------------------------------------------------------------------
+// Staging.  Every thread stages one activation task and one weight task per
+// super-block.  Activations: tau = tid % 64 is the token, p = tid / 64 the
+// pair of pad40 blocks (chunks 2p, 2p+1).  Weights: row = tid % 64 and
+// part = tid / 64 (0..3), a quarter of the super-block's quants:
+//   q4_K: nibble group `part` -> chunks 2part (low nibbles), 2part+1 (high);
+//   q6_K: half h = part/2 and pair pp = part%2 -> chunks 4h+pp and 4h+pp+2,
+//         which share the same ql bytes (low / high nibble) and qh bytes.
+// Lanes of a wave walk consecutive rows, so LDS writes are free of bank
+// conflicts.  Rows past the end are clamped to the last valid one: the loads
+// stay unconditional and a clamped row only feeds outputs never stored.
+// ---------------------------------------------------------------------------
+template <int QT, bool WEXP>
+struct Raw {
+    static constexpr int NQ = QT == 4 ? 2 : 4;
+    u32x4 a[5];    // two pad40 blocks of one token (80 bytes)
+    u32x4 h;       // q4_K header (d, dmin, 12 scale bytes) | q6_K: 16 int8 scales
+    u32x4 q[NQ];   // q4_K: 32 nibble bytes | q6_K raw: ql 32 B, qh 32 B | W_exp: 2 x 32 B
+    uint32_t d;    // q6_K fp16 d (low half)
+};
+
+struct Src {
+    const uint8_t *a;    // token slab start of this thread's block pair
+    const uint8_t *w;    // weight row start (raw blocks)
+    const uint8_t *x;    // W_exp row start (q6_K dense arm)
+    int64_t wstep;       // bytes per super-block along w
+};
+
+template <int QT, bool WEXP>
+__device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t jw0)
 {
+    Src s;
     const int tid = threadIdx.x;
-    const int tau = tid >> 2, p = tid & 3;
-    uint32_t w[20];
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-        w[4 * k + 0] = r.a[k][0];
-        w[4 * k + 1] = r.a[k][1];
-        w[4 * k + 2] = r.a[k][2];
-        w[4 * k + 3] = r.a[k][3];
-    }
-    const int sl = (tau & 32) + row_slot(tau & 31);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int c = 2 * p + k;
-        const uint32_t *b = w + 10 * k;
-        s.ad[c][sl] = (uint16_t)(b[0] & 0xffffu);
-        u32x4 lo = {b[1], b[2], b[3], b[4]};
-        u32x4 hi = {b[5], b[6], b[7], b[8]};
-        *reinterpret_cast<u32x4 *>(&s.a[c][tau][16 * (0 ^ swz(tau))]) = lo;
-        *reinterpret_cast<u32x4 *>(&s.a[c][tau][16 * (1 ^ swz(tau))]) = hi;
-        if constexpr (QT == 4) s.as[c][tau] = __builtin_bit_cast(float, b[9]);
-    }
+    const int64_t nb32 = g.id / 32, nsb = g.id / 256;
+    const int64_t t = min(tw0 + (tid & 63), g.nt - 1);
+    s.a = g.q8 + (t * nb32 + 2 * (tid >> 6)) * 40;
+    const int64_t j = min(jw0 + (tid & 63), g.od - 1);
+    s.wstep = QT == 4 ? 144 : g.bstride;
+    s.w = g.W + j * nsb * s.wstep;
+    s.x = WEXP ? g.Wexp + j * g.id : nullptr;
+    return s;
 }
 
-// q4_K weights: thread -> (row r = tid/2, half g2 = tid%2: nibble groups 2g2, 2g2+1)
-__device__ __forceinline__ void load_b(Regs<4, false> &r, const MmqArgs &g, int64_t jw0, int64_t sb)
+template <int QT, bool WEXP>
+__device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t sb)
 {
-    const int tid = threadIdx.x;
-    const int row = tid >> 1, g2 = tid & 1;
-    const int64_t j = jw0 + row;
-    const int64_t nsb = g.id / 256;
-    if (j < g.od) {
-        const uint8_t *blk = g.W + (j * nsb + sb) * 144;
+    const int part = threadIdx.x >> 6;
+    const uint8_t *pa = s.a + sb * 320;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) r.a[k] = ld16(pa + 16 * k);
+    const uint8_t *blk = s.w + sb * s.wstep;
+    if constexpr (QT == 4) {
         r.h = ld16(blk);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) r.q[k] = ld16(blk + 16 + 64 * g2 + 16 * k);
+        r.q[0] = ld16(blk + 16 + 32 * part);
+        r.q[1] = ld16(blk + 32 + 32 * part);
     } else {
-        r.h = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) r.q[k] = u32x4{0, 0, 0, 0};
-    }
-}
-
-__device__ __forceinline__ void store_b(Stage<4> &s, const Regs<4, false> &r)
-{
-    const int tid = threadIdx.x;
-    const int row = tid >> 1, g2 = tid & 1;
-    const int sw = swz(row);
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-        const int grp = 2 * g2 + gg;          // nibble group: chunks 2grp (low), 2grp+1 (high)
-        const u32x4 w0 = r.q[2 * gg], w1 = r.q[2 * gg + 1];
-        u32x4 lo0 = w0 & 0x0F0F0F0Fu, lo1 = w1 & 0x0F0F0F0Fu;
-        u32x4 hi0 = (w0 >> 4) & 0x0F0F0F0Fu, hi1 = (w1 >> 4) & 0x0F0F0F0Fu;
-        *reinterpret_cast<u32x4 *>(&s.b[2 * grp][row][16 * (0 ^ sw)]) = lo0;
-        *reinterpret_cast<u32x4 *>(&s.b[2 * grp][row][16 * (1 ^ sw)]) = lo1;
-        *reinterpret_cast<u32x4 *>(&s.b[2 * grp + 1][row][16 * (0 ^ sw)]) = hi0;
-        *reinterpret_cast<u32x4 *>(&s.b[2 * grp + 1][row][16 * (1 ^ sw)]) = hi1;
-    }
-    uint8_t S[12];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const uint32_t v = r.h[1 + k];
-        S[4 * k + 0] = v & 0xff;
-        S[4 * k + 1] = (v >> 8) & 0xff;
-        S[4 * k + 2] = (v >> 16) & 0xff;
-        S[4 * k + 3] = v >> 24;
-    }
-    const float d = h2f(r.h[0]), dmin = h2f(r.h[0] >> 16);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int b = 4 * g2 + k;
-        int sc, m;
-        q4_scale_min(S, b, sc, m);
-        s.bs[b][row] = d * (float)sc;
-        s.bm[b][row] = dmin * (float)m;
-    }
-}
-
-// q6_K weights: thread -> (row r = tid/2, half h = tid%2: chunks 4h..4h+3)
-template <bool WEXP>
-__device__ __forceinline__ void load_b(Regs<6, WEXP> &r, const MmqArgs &g, int64_t jw0, int64_t sb)
-{
-    const int tid = threadIdx.x;
-    const int row = tid >> 1, h = tid & 1;
-    const int64_t j = jw0 + row;
-    const int64_t nsb = g.id / 256;
-    if (j < g.od) {
-        const uint8_t *blk = g.W + j * nsb * g.bstride + sb * g.bstride;
+        const int h = part >> 1, pp = part & 1;
         if constexpr (WEXP) {
-            const uint8_t *src = g.Wexp + j * g.id + 256 * sb + 128 * h;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) r.q[k] = ld16(src + 16 * k);
+            // chunks 4h+pp and 4h+pp+2 of the dense plane
+            const uint8_t *px = s.x + sb * 256 + 128 * h + 32 * pp;
+            r.q[0] = ld16(px);
+            r.q[1] = ld16(px + 16);
+            r.q[2] = ld16(px + 64);
+            r.q[3] = ld16(px + 80);
         } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) r.q[k] = ld16(blk + 64 * h + 16 * k);
-#pragma unroll
-            for (int k = 0; k < 2; ++k) r.q[4 + k] = ld16(blk + 128 + 32 * h + 16 * k);
+            r.q[0] = ld16(blk + 64 * h + 32 * pp);        // ql bytes of quarters pp, pp+2
+            r.q[1] = ld16(blk + 64 * h + 32 * pp + 16);
+            r.q[2] = ld16(blk + 128 + 32 * h);            // qh bytes of this half
+            r.q[3] = ld16(blk + 128 + 32 * h + 16);
         }
-        r.sc = ld16(blk + 192);
+        r.h = ld16(blk + 192);
         r.d = *reinterpret_cast<const uint32_t *>(blk + 208);
-    } else {
-#pragma unroll
-        for (int k = 0; k < (WEXP ? 8 : 6); ++k) r.q[k] = u32x4{0, 0, 0, 0};
-        r.sc = u32x4{0, 0, 0, 0};
-        r.d = 0;
     }
 }
 
-template <bool WEXP>
-__device__ __forceinline__ void store_b(Stage<6> &s, const Regs<6, WEXP> &r)
+template <int QT, bool WEXP>
+__device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
 {
     const int tid = threadIdx.x;
-    const int row = tid >> 1, h = tid & 1;
+    const int row = tid & 63, part = tid >> 6;
     const int sw = swz(row);
+    // activations: token row, chunks 2part, 2part+1
+    {
+        const int sl = (row & 32) + row_slot(row & 31);
+        uint32_t w[20];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-        const int c = 4 * h + qq;
-        u32x4 o[2];
-        if constexpr (WEXP) {
-            o[0] = r.q[2 * qq];
-            o[1] = r.q[2 * qq + 1];
-        } else {
+        for (int k = 0; k < 5; ++k)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+            for (int e = 0; e < 4; ++e) w[4 * k + e] = r.a[k][e];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int k = 4 * hh + e;   // output dword 0..7 of the chunk
-                    const uint32_t qlw = r.q[2 * (qq & 1) + (k >> 2)][k & 3];
-                    const uint32_t qhw = r.q[4 + (k >> 2)][k & 3];
-                    o[hh][e] = q6_centred(qlw, qhw, qq);
-                }
+        for (int k = 0; k < 2; ++k) {
+            const int c = 2 * part + k;
+            const uint32_t *b = w + 10 * k;
+            s.ad[c][sl] = h2f(b[0]);
+            st16(&s.a[c][row][16 * (0 ^ sw)], u32x4{b[1], b[2], b[3], b[4]});
+            st16(&s.a[c][row][16 * (1 ^ sw)], u32x4{b[5], b[6], b[7], b[8]});
+            if constexpr (QT == 4) s.as[c][row] = __builtin_bit_cast(float, b[9]);
         }
-        *reinterpret_cast<u32x4 *>(&s.b[c][row][16 * (0 ^ sw)]) = o[0];
-        *reinterpret_cast<u32x4 *>(&s.b[c][row][16 * (1 ^ sw)]) = o[1];
     }
-    const float d = h2f(r.d);
+    if constexpr (QT == 4) {
+        // nibble group `part` -> chunks 2part (low nibbles), 2part+1 (high)
+        const u32x4 w0 = r.q[0], w1 = r.q[1];
+        st16(&s.b[2 * part][row][16 * (0 ^ sw)], w0 & 0x0F0F0F0Fu);
+        st16(&s.b[2 * part][row][16 * (1 ^ sw)], w1 & 0x0F0F0F0Fu);
+        st16(&s.b[2 * part + 1][row][16 * (0 ^ sw)], (w0 >> 4) & 0x0F0F0F0Fu);
+        st16(&s.b[2 * part + 1][row][16 * (1 ^ sw)], (w1 >> 4) & 0x0F0F0F0Fu);
+        // scale/min of sub-blocks 2part, 2part+1 from the twelve packed bytes
+        // S[0..11] = header bytes 4..15.
+        const float d = h2f(r.h[0]), dmin = h2f(r.h[0] >> 16);
+        const uint32_t hi = part >= 2 ? 0xffffffffu : 0u;    // sub-blocks 4..7
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-        const int c = 4 * h + qq;
-        const uint32_t v = r.sc[c >> 1];            // scale bytes 2c, 2c+1
-        const int sh = 16 * (c & 1);
-        const float s0 = (float)(int8_t)((v >> sh) & 0xff);
-        const float s1 = (float)(int8_t)((v >> (sh + 8)) & 0xff);
-        s.bs[c][row][0] = d * s0;
-        s.bs[c][row][1] = d * s1;
+        for (int k = 0; k < 2; ++k) {
+            const int b = 2 * part + k;
+            const int sh = 8 * (b & 3);                         // byte (b mod 4) of each group
+            const uint32_t s0 = (r.h[1] >> sh) & 0xff;          // S[b mod 4]
+            const uint32_t s1 = (r.h[2] >> sh) & 0xff;          // S[4 + b mod 4]
+            const uint32_t s2 = (r.h[3] >> sh) & 0xff;          // S[8 + b mod 4]
+            const uint32_t sc = (hi & ((s2 & 15) | ((s0 >> 6) << 4))) | (~hi & (s0 & 63));
+            const uint32_t m = (hi & ((s2 >> 4) | ((s1 >> 6) << 4))) | (~hi & (s1 & 63));
+            s.bs[b][row] = d * (float)sc;
+            s.bm[b][row] = dmin * (float)m;
+        }
+    } else {
+        const int h = part >> 1, pp = part & 1;
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+            const int qq = pp + 2 * z;          // quarter of the half
+            const int c = 4 * h + qq;
+            u32x4 o[2];
+            if constexpr (WEXP) {
+                o[0] = r.q[2 * z];
+                o[1] = r.q[2 * z + 1];
+            } else {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)   // output dword 4h2+e of the chunk
+                        o[h2][e] = q6_centred(r.q[h2][e], r.q[2 + h2][e], qq);
+            }
+            st16(&s.b[c][row][16 * (0 ^ sw)], o[0]);
+            st16(&s.b[c][row][16 * (1 ^ sw)], o[1]);
+            const uint32_t v = r.h[c >> 1];             // scale bytes 2c, 2c+1
+            const int sh = 16 * (c & 1);
+            const float d = h2f(r.d);
+            s.bs[c][row][0] = d * (float)(int8_t)((v >> sh) & 0xff);
+            s.bs[c][row][1] = d * (float)(int8_t)((v >> (sh + 8)) & 0xff);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-wave compute
+// ---------------------------------------------------------------------------
+template <int QT>
+struct Ab {                          // MFMA operands of one chunk
+    i32x4 a0, a1;                    // q4_K: a0 = activation operand; q6_K: the two K halves
+    i32x4 b;                         // weight operand
+};
+
+template <int QT>
+struct Sc {                          // epilogue scales of one chunk
+    float x;                         // activation scale of token row mfma_row(lane % 16, half)
+    float w0, w1;                    // weight scale (q6_K: of both sub-blocks)
+    float am, bm;                    // q4_K min-term operands (odd chunks)
+};
+
+template <int QT>
+struct ChunkD {                      // MFMA results of one chunk
+    i32x16 v[QT == 4 ? 1 : 2];
+};
+
+struct Lane {
+    int ta, hh, wt, jb, l16;
+};
+
+template <int QT>
+__device__ __forceinline__ void load_ab(Ab<QT> &o, const Stage<QT> &s, int c, const Lane &L)
+{
+    const i32x4 av = *reinterpret_cast<const i32x4 *>(&s.a[c][L.ta][16 * (L.hh ^ swz(L.ta))]);
+    if constexpr (QT == 4) {
+        o.a0 = av;
+    } else {
+        const i32x4 zero = {0, 0, 0, 0};
+        o.a0 = L.hh ? zero : av;     // first 16 elements of the chunk
+        o.a1 = L.hh ? av : zero;     // last 16
+    }
+    o.b = *reinterpret_cast<const i32x4 *>(&s.b[c][L.jb][16 * (L.hh ^ swz(L.jb))]);
+}
+
+template <int QT>
+__device__ __forceinline__ void load_sc(Sc<QT> &o, const Stage<QT> &s, int c, const Lane &L)
+{
+    o.x = s.ad[c][32 * L.wt + 16 * L.hh + L.l16];
+    if constexpr (QT == 4) {
+        o.w0 = s.bs[c][L.jb];
+        if (c & 1) {                 // min term of chunks c-1, c: k = lane half
+            const int ck = c - 1 + L.hh;
+            o.am = -s.as[ck][L.ta];
+            o.bm = s.bm[ck][L.jb];
+        }
+    } else {
+        o.w0 = s.bs[c][L.jb][0];
+        o.w1 = s.bs[c][L.jb][1];
+    }
+}
+
+template <int QT>
+__device__ __forceinline__ ChunkD<QT> mfma_chunk(const Ab<QT> &o, const i32x16 &bias)
+{
+    ChunkD<QT> r;
+    r.v[0] = mfma_i8(o.a0, o.b, bias);
+    if constexpr (QT == 6) r.v[1] = mfma_i8(o.a1, o.b, bias);
+    return r;
+}
+
+// acc += bcast_i(x) * u, where bcast_i hands every lane of a 16-lane row the
+// value x holds in lane i of that row (DPP row_newbcast).  A lane loads the
+// scale of token row mfma_row(lane % 16, lane / 32), so register i of every
+// lane sees the scale of its own row mfma_row(i, lane / 32).  The DPP source
+// x comes straight from an LDS load; the leading s_nop covers the DPP
+// read-after-VALU-write window should x ever be produced by a VALU move.
+template <int I>
+__device__ __forceinline__ float fmac_bcast(float acc, float x, float u)
+{
+    if constexpr (I == 0)
+        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf"
+            : "+v"(acc) : "v"(x), "v"(u));
+    else
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+            : "+v"(acc) : "v"(x), "v"(u), "i"(I));
+    return acc;
+}
+
+template <int... I>
+__device__ __forceinline__ void scale_rows(f32x16 &acc, const i32x16 &D, float w, float nw, float x,
+                                           std::integer_sequence<int, I...>)
+{
+    ((acc[I] = fmac_bcast<I>(acc[I], x, __builtin_fmaf(as_float(D[I]), w, nw))), ...);
+}
+
+template <int QT, int MODE>
+__device__ __forceinline__ void epilogue(const ChunkD<QT> &D, const Sc<QT> &o, f32x16 &acc,
+                                         const MmqArgs &g, int64_t tw0, int64_t j, int64_t sb, int c,
+                                         const Lane &L)
+{
+    if constexpr (MODE == 0) {
+        constexpr auto rows = std::make_integer_sequence<int, 16>{};
+        scale_rows(acc, D.v[0], o.w0, -MAGIC_F * o.w0, o.x, rows);
+        if constexpr (QT == 6) scale_rows(acc, D.v[1], o.w1, -MAGIC_F * o.w1, o.x, rows);
+    } else {
+        const int64_t nsb = g.id / 256;
+        const int64_t nsub = (QT == 4 ? 8 : 16) * nsb;
+        const int64_t sub = QT == 4 ? 8 * sb + c : 2 * (8 * sb + c);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t t = tw0 + 32 * L.wt + mfma_row(i, L.hh);
+            if (t < g.t1 && j < g.j1) {
+                int32_t *dst = g.P + ((t - g.t0) * (g.j1 - g.j0) + (j - g.j0)) * nsub + sub;
+                dst[0] = D.v[0][i] - MAGIC_I;
+                if constexpr (QT == 6) dst[1] = D.v[1][i] - MAGIC_I;
+            }
+        }
     }
 }
 
@@ -278,152 +375,90 @@ __device__ __forceinline__ void store_b(Stage<6> &s, const Regs<6, WEXP> &r)
 // the kernel
 // ---------------------------------------------------------------------------
 template <int QT, bool WEXP, int MODE>
-__global__ __launch_bounds__(NTHR, 1) void mmq_kernel(MmqArgs g)
+__global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 {
     __shared__ Stage<QT> st[2];
 
-    const int bt = blockIdx.x % g.nbt;
-    const int bj = blockIdx.x / g.nbt;
+    // XCD-aware numbering: consecutive blocks go round-robin to the 8 XCDs,
+    // so hand each XCD a contiguous run of tile indices.
+    const int G = gridDim.x, b = blockIdx.x;
+    const int q = G / 8, r = G % 8, x = b % 8;
+    const int tile = x * q + min(x, r) + b / 8;
+    const int bt = tile % g.nbt;
+    const int bj = tile / g.nbt;
     const int64_t tw0 = g.t0 + (int64_t)TT * bt;   // workgroup tile origin
     const int64_t jw0 = g.j0 + (int64_t)TJ * bj;
     const int64_t nsb = g.id / 256;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wt = wave & 1;          // 32-token group of this wave
-    const int wj = wave >> 1;         // 64-row group of this wave
-    const int l32 = lane & 31;
-    const int hh = lane >> 5;
-    const int ta = 32 * wt + l32;     // token (tile-local) this lane loads for MFMA a
-    const int jb[2] = {64 * wj + l32, 64 * wj + 32 + l32};   // weight rows of the lane
+    Lane L;
+    L.wt = wave & 1;                       // 32-token group of this wave
+    L.hh = lane >> 5;
+    L.ta = 32 * L.wt + (lane & 31);        // token (tile-local) this lane feeds to MFMA a
+    L.jb = 32 * (wave >> 1) + (lane & 31); // weight row (tile-local) of the lane
+    L.l16 = lane & 15;
+    const int64_t j = jw0 + L.jb;
 
     i32x16 bias;
 #pragma unroll
     for (int i = 0; i < 16; ++i) bias[i] = MAGIC_I;
-    f32x16 acc[2], accm[2];
+    f32x16 acc, accm;
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            acc[n][i] = 0.0f;
-            accm[n][i] = 0.0f;
-        }
+    for (int i = 0; i < 16; ++i) {
+        acc[i] = 0.0f;
+        accm[i] = 0.0f;
+    }
 
-    Regs<QT, WEXP> rg;
-    load_a(rg, g, tw0, 0);
-    load_b(rg, g, jw0, 0);
-    store_a<QT>(st[0], rg);
-    store_b(st[0], rg);
+    const Src src = make_src<QT, WEXP>(g, tw0, jw0);
+    Raw<QT, WEXP> rw;
+    load_raw(rw, src, 0);
+    store_raw(st[0], rw);
     __syncthreads();
 
     for (int64_t sb = 0; sb < nsb; ++sb) {
-        Stage<QT> &s = st[sb & 1];
+        const Stage<QT> &s = st[sb & 1];
         const bool more = sb + 1 < nsb;
-        if (more) {
-            load_a(rg, g, tw0, sb + 1);
-            load_b(rg, g, jw0, sb + 1);
-        }
-#pragma unroll 2
+        if (more) load_raw(rw, src, sb + 1);
+
+        // Operand rings, three deep: chunk c+2's MFMA operands and scales are
+        // fetched from LDS while chunk c's epilogue runs.
+        Ab<QT> ab[3];
+        Sc<QT> sc[3];
+        ChunkD<QT> dd[2];
+        load_ab(ab[0], s, 0, L);
+        load_sc(sc[0], s, 0, L);
+        load_ab(ab[1], s, 1, L);
+        load_sc(sc[1], s, 1, L);
+        dd[0] = mfma_chunk(ab[0], bias);
+#pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const i32x4 av = *reinterpret_cast<const i32x4 *>(&s.a[c][ta][16 * (hh ^ swz(ta))]);
-            i32x4 bv[2];
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                bv[n] = *reinterpret_cast<const i32x4 *>(&s.b[c][jb[n]][16 * (hh ^ swz(jb[n]))]);
-            // fp16 activation scales of this lane's 16 token rows, register order
-            _Float16 da[16];
-            {
-                const u32x4 d0 = *reinterpret_cast<const u32x4 *>(&s.ad[c][32 * wt + 16 * hh]);
-                const u32x4 d1 = *reinterpret_cast<const u32x4 *>(&s.ad[c][32 * wt + 16 * hh + 8]);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    da[2 * k] = __builtin_bit_cast(_Float16, (uint16_t)(d0[k] & 0xffff));
-                    da[2 * k + 1] = __builtin_bit_cast(_Float16, (uint16_t)(d0[k] >> 16));
-                    da[8 + 2 * k] = __builtin_bit_cast(_Float16, (uint16_t)(d1[k] & 0xffff));
-                    da[8 + 2 * k + 1] = __builtin_bit_cast(_Float16, (uint16_t)(d1[k] >> 16));
-                }
+            if (c + 2 < NCH) {
+                load_ab(ab[(c + 2) % 3], s, c + 2, L);
+                load_sc(sc[(c + 2) % 3], s, c + 2, L);
             }
-            if constexpr (QT == 4) {
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    const i32x16 D = mfma_i8(av, bv[n], bias);
-                    if constexpr (MODE == 0) {
-                        const float w = s.bs[c][jb[n]];
-                        const float nw = -MAGIC_F * w;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const float u = __builtin_fmaf(as_float(D[i]), w, nw);
-                            acc[n][i] = __builtin_fmaf(u, (float)da[i], acc[n][i]);
-                        }
-                    } else {
-                        const int64_t j = jw0 + jb[n];
-                        const int64_t nsub = 8 * nsb, sub = 8 * sb + c;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int64_t t = tw0 + 32 * wt + mfma_row(i, hh);
-                            if (t < g.t1 && j < g.j1)
-                                g.P[((t - g.t0) * (g.j1 - g.j0) + (j - g.j0)) * nsub + sub] = D[i] - MAGIC_I;
-                        }
-                    }
-                }
-                if constexpr (MODE == 0) {
-                    if (c & 1) {   // min term for chunks c-1, c on the fp32 MFMA
-                        const int ck = c - 1 + hh;
-                        const float am = -s.as[ck][ta];
-#pragma unroll
-                        for (int n = 0; n < 2; ++n) accm[n] = mfma_f32(am, s.bm[ck][jb[n]], accm[n]);
-                    }
-                }
-            } else {
-                const i32x4 zero = {0, 0, 0, 0};
-                const i32x4 a0 = hh ? zero : av;   // first 16 elements of the chunk
-                const i32x4 a1 = hh ? av : zero;   // last 16
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    const i32x16 D0 = mfma_i8(a0, bv[n], bias);
-                    const i32x16 D1 = mfma_i8(a1, bv[n], bias);
-                    if constexpr (MODE == 0) {
-                        const float w0 = s.bs[c][jb[n]][0], w1 = s.bs[c][jb[n]][1];
-                        const float nw0 = -MAGIC_F * w0, nw1 = -MAGIC_F * w1;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const float u0 = __builtin_fmaf(as_float(D0[i]), w0, nw0);
-                            acc[n][i] = __builtin_fmaf(u0, (float)da[i], acc[n][i]);
-                            const float u1 = __builtin_fmaf(as_float(D1[i]), w1, nw1);
-                            acc[n][i] = __builtin_fmaf(u1, (float)da[i], acc[n][i]);
-                        }
-                    } else {
-                        const int64_t j = jw0 + jb[n];
-                        const int64_t nsub = 16 * nsb, sub = 2 * (8 * sb + c);
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int64_t t = tw0 + 32 * wt + mfma_row(i, hh);
-                            if (t < g.t1 && j < g.j1) {
-                                int32_t *dst = g.P + ((t - g.t0) * (g.j1 - g.j0) + (j - g.j0)) * nsub + sub;
-                                dst[0] = D0[i] - MAGIC_I;
-                                dst[1] = D1[i] - MAGIC_I;
-                            }
-                        }
-                    }
-                }
+            ChunkD<QT> &cur = dd[c & 1];
+            if (c + 1 < NCH) {
+                ChunkD<QT> &nxt = dd[(c + 1) & 1];
+                nxt = mfma_chunk(ab[(c + 1) % 3], bias);
+                pin_after(cur.v[0], nxt.v[QT == 4 ? 0 : 1]);   // issue MFMA c+1 first
+                if constexpr (QT == 6) pin(cur.v[1]);
             }
+            epilogue<QT, MODE>(cur, sc[c % 3], acc, g, tw0, j, sb, c, L);
+            if constexpr (QT == 4 && MODE == 0)
+                if (c & 1) accm = mfma_f32(sc[c % 3].am, sc[c % 3].bm, accm);
+            if constexpr (MODE == 0) pin(acc);                  // epilogue c done here
         }
-        if (more) {
-            store_a<QT>(st[(sb + 1) & 1], rg);
-            store_b(st[(sb + 1) & 1], rg);
-        }
+        if (more) store_raw(st[(sb + 1) & 1], rw);
         __syncthreads();
     }
 
     if constexpr (MODE == 0) {
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int64_t j = jw0 + jb[n];
-            if (j >= g.j1) continue;
+        if (j < g.j1) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int64_t t = tw0 + 32 * wt + mfma_row(i, hh);
-                if (t < g.t1) g.y[t * g.ldy + j] = acc[n][i] + accm[n][i];
+                const int64_t t = tw0 + 32 * L.wt + mfma_row(i, L.hh);
+                if (t < g.t1) g.y[t * g.ldy + j] = acc[i] + accm[i];
             }
         }
     }
@@ -445,28 +480,28 @@ static int launch(MmqArgs g, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-int launch_mmq(const MmqLaunch &L, hipStream_t stream)
+int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
 {
     MmqArgs g;
-    g.W = static_cast<const uint8_t *>(L.W);
-    g.Wexp = reinterpret_cast<const uint8_t *>(L.Wexp);
-    g.q8 = static_cast<const uint8_t *>(L.q8);
-    g.y = L.y;
-    g.P = L.P;
-    g.bstride = L.bstride;
-    g.od = L.od;
-    g.id = L.id;
-    g.nt = L.nt;
-    g.ldy = L.ldy;
-    g.t0 = L.t0;
-    g.t1 = L.t1;
-    g.j0 = L.j0;
-    g.j1 = L.j1;
+    g.W = static_cast<const uint8_t *>(Lc.W);
+    g.Wexp = reinterpret_cast<const uint8_t *>(Lc.Wexp);
+    g.q8 = static_cast<const uint8_t *>(Lc.q8);
+    g.y = Lc.y;
+    g.P = Lc.P;
+    g.bstride = Lc.bstride;
+    g.od = Lc.od;
+    g.id = Lc.id;
+    g.nt = Lc.nt;
+    g.ldy = Lc.ldy;
+    g.t0 = Lc.t0;
+    g.t1 = Lc.t1;
+    g.j0 = Lc.j0;
+    g.j1 = Lc.j1;
     g.nbt = 0;
-    const bool part = L.P != nullptr;
-    if (L.qtype == 4)
+    const bool part = Lc.P != nullptr;
+    if (Lc.qtype == 4)
         return part ? launch<4, false, 1>(g, stream) : launch<4, false, 0>(g, stream);
-    if (L.Wexp)
+    if (Lc.Wexp)
         return part ? launch<6, true, 1>(g, stream) : launch<6, true, 0>(g, stream);
     return part ? launch<6, false, 1>(g, stream) : launch<6, false, 0>(g, stream);
 }
