@@ -50,23 +50,34 @@ constexpr int NCH = 8;    // 32-element chunks per super-block
 template <int QT>
 struct Stage;
 
+// Activations arrive by direct global->LDS copies (load_act): the two
+// 16-byte quant halves of every pad40 block, and the d and ssum dwords as
+// they are in the block.  Weights are decoded on the way in (store_raw).
 template <>
 struct Stage<4> {
-    uint8_t a[NCH][TT][32];     // activation quants (16-byte halves swizzled)
-    float ad[NCH][TT];          // activation d (fp16 value as fp32), row_slot order
-    float as[NCH][TT];          // activation ssum
+    __attribute__((aligned(16))) uint8_t a[NCH][TT][32];   // activation quants (halves swizzled)
+    uint32_t ad[TT][NCH];       // activation block dword 0 (fp16 d in the low half), slot ad_slot
+    float as[TT][NCH];          // activation ssum, same slots
     uint8_t b[NCH][TJ][32];     // weight nibbles 0..15 as int8
     float bs[NCH][TJ];          // d * sc
     float bm[NCH][TJ];          // dmin * m
 };
 
+// q6_K: row TT of every chunk plane of a is all zero.  Each 16-element
+// sub-block has its own MFMA, which must see zeros in the lanes that carry
+// the other half of the chunk; those lanes read the zero row instead of
+// selecting zeros with VALU instructions.
 template <>
 struct Stage<6> {
-    uint8_t a[NCH][TT][32];
-    float ad[NCH][TT];
+    __attribute__((aligned(16))) uint8_t a[NCH][TT + 1][32];
+    uint32_t ad[TT][NCH];
     uint8_t b[NCH][TJ][32];     // centred int8 weights
     float bs[NCH][TJ][2];       // d * sc of the two 16-element sub-blocks
 };
+
+// Chunk c of token t sits in slot c ^ ((t >> 3) & 7) of its ad / as row, so
+// that 32 consecutive tokens reading one chunk hit 32 distinct banks.
+__device__ __forceinline__ int ad_slot(int t, int c) { return c ^ ((t >> 3) & 7); }
 
 // The 16-byte half h of row r is stored at half h ^ swz(r).  An LDS access
 // phase serves 8 (32 banks) or 16 (64 banks) lanes reading 16 bytes of
@@ -107,28 +118,29 @@ template <typename T, typename U>
 __device__ __forceinline__ void pin_after(T &x, const U &y) { asm volatile("" : "+v"(x) : "v"(y)); }
 
 // ---------------------------------------------------------------------------
-// Staging.  Every thread stages one activation task and one weight task per
-// super-block.  Activations: tau = tid % 64 is the token, p = tid / 64 the
-// pair of pad40 blocks (chunks 2p, 2p+1).  Weights: row = tid % 64 and
-// part = tid / 64 (0..3), a quarter of the super-block's quants:
+// Staging.  Activations are copied straight into LDS (make_src, load_act).
+// Weights go through registers and are decoded on the way into LDS: row =
+// 16 * wave + lane % 16 and part = (lane / 16) % 4, a quarter of the
+// super-block's quants:
 //   q4_K: nibble group `part` -> chunks 2part (low nibbles), 2part+1 (high);
 //   q6_K: half h = part/2 and pair pp = part%2 -> chunks 4h+pp and 4h+pp+2,
 //         which share the same ql bytes (low / high nibble) and qh bytes.
-// Lanes of a wave walk consecutive rows, so LDS writes are free of bank
-// conflicts.  Rows past the end are clamped to the last valid one: the loads
-// stay unconditional and a clamped row only feeds outputs never stored.
+// Each 16-lane group walks 16 consecutive rows, so the LDS writes are free of
+// bank conflicts.  Rows and tokens past the end are clamped to the last valid
+// one: the loads stay unconditional and a clamped row only feeds outputs that
+// are never stored.
 // ---------------------------------------------------------------------------
 template <int QT, bool WEXP>
 struct Raw {
     static constexpr int NQ = QT == 4 ? 2 : 4;
-    u32x4 a[5];    // two pad40 blocks of one token (80 bytes)
     u32x4 h;       // q4_K header (d, dmin, 12 scale bytes) | q6_K: 16 int8 scales
     u32x4 q[NQ];   // q4_K: 32 nibble bytes | q6_K raw: ql 32 B, qh 32 B | W_exp: 2 x 32 B
     uint32_t d;    // q6_K fp16 d (low half)
 };
 
 struct Src {
-    const uint8_t *a;    // token slab start of this thread's block pair
+    const uint8_t *aq[2]; // quant-half source of this lane, token halves 0/1 of the tile
+    const uint8_t *ad[2]; // block source for this lane's d / ssum copies
     const uint8_t *w;    // weight row start (raw blocks)
     const uint8_t *x;    // W_exp row start (q6_K dense arm)
     int64_t wstep;       // bytes per super-block along w
@@ -140,22 +152,69 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
     Src s;
     const int tid = threadIdx.x;
     const int64_t nb32 = g.id / 32, nsb = g.id / 256;
-    const int64_t t = min(tw0 + (tid & 63), g.nt - 1);
-    s.a = g.q8 + (t * nb32 + 2 * (tid >> 6)) * 40;
-    const int64_t j = min(jw0 + (tid & 63), g.od - 1);
+    // Activation copies (one super-block = 16 quant copies of 1 KB and 8 (q6_K)
+    // or 16 (q4_K) dword copies of 256 bytes per workgroup).  Quant copy q of
+    // Stage::a (wave w issues q = 4w .. 4w+3) fills a[c][32*th .. +31] with
+    // c = q / 2, th = q % 2: lane l brings half h' = l % 2 of token
+    // 32*th + l/2, i.e. quant bytes 16*(h' ^ swz(t)) .. +15 of its block.
+    // Dword copy q of ad / as (wave w issues q = 2w, 2w+1) fills tokens
+    // 8q .. 8q+7: lane l fills slot l % 8 of token 8q + l/8, i.e. brings the
+    // block c with ad_slot(t, c) = l % 8 (c = (l % 8) ^ q).
+    {
+        const int l = tid & 63, w = tid >> 6;
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            const int t = 32 * th + (l >> 1);
+            const int64_t tg = min(tw0 + t, g.nt - 1);
+            s.aq[th] = g.q8 + tg * nb32 * 40 + 4 + 16 * ((l & 1) ^ swz(t));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = 8 * (2 * w + i) + (l >> 3);
+            const int64_t tg = min(tw0 + t, g.nt - 1);
+            s.ad[i] = g.q8 + (tg * nb32 + ((l & 7) ^ (t >> 3))) * 40;
+        }
+    }
+    // Weight staging: lanes l and l+16k of a wave take rows 16w + l%16, so a
+    // load covers 16 rows (not 64) and the LDS writes stay conflict free.
+    const int64_t j = min(jw0 + 16 * (tid >> 6) + (tid & 15), g.od - 1);
     s.wstep = QT == 4 ? 144 : g.bstride;
     s.w = g.W + j * nsb * s.wstep;
     s.x = WEXP ? g.Wexp + j * g.id : nullptr;
     return s;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// Direct global->LDS copies of super-block sb's activations into stage st.
+// The data lands asynchronously; a vmcnt(0) wait plus a barrier must come
+// before any wave reads it.
+template <int QT>
+__device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb)
+{
+    const int w = threadIdx.x >> 6;
+    const int64_t off = sb * 320;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = 4 * w + i, c = q >> 1;
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(s.aq[i & 1] + off + 40 * c),
+                                         (lds_void_t *)(&st.a[c][32 * (q & 1)][0]), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = 2 * w + i;
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(s.ad[i] + off), (lds_void_t *)(&st.ad[8 * q][0]), 4, 0, 0);
+        if constexpr (QT == 4)
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(s.ad[i] + off + 36), (lds_void_t *)(&st.as[8 * q][0]),
+                                             4, 0, 0);
+    }
+}
+
 template <int QT, bool WEXP>
 __device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t sb)
 {
-    const int part = threadIdx.x >> 6;
-    const uint8_t *pa = s.a + sb * 320;
-#pragma unroll
-    for (int k = 0; k < 5; ++k) r.a[k] = ld16(pa + 16 * k);
+    const int part = (threadIdx.x >> 4) & 3;
     const uint8_t *blk = s.w + sb * s.wstep;
     if constexpr (QT == 4) {
         r.h = ld16(blk);
@@ -185,26 +244,8 @@ template <int QT, bool WEXP>
 __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
 {
     const int tid = threadIdx.x;
-    const int row = tid & 63, part = tid >> 6;
+    const int row = 16 * (tid >> 6) + (tid & 15), part = (tid >> 4) & 3;
     const int sw = swz(row);
-    // activations: token row, chunks 2part, 2part+1
-    {
-        const int sl = (row & 32) + row_slot(row & 31);
-        uint32_t w[20];
-#pragma unroll
-        for (int k = 0; k < 5; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[4 * k + e] = r.a[k][e];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int c = 2 * part + k;
-            const uint32_t *b = w + 10 * k;
-            s.ad[c][sl] = h2f(b[0]);
-            st16(&s.a[c][row][16 * (0 ^ sw)], u32x4{b[1], b[2], b[3], b[4]});
-            st16(&s.a[c][row][16 * (1 ^ sw)], u32x4{b[5], b[6], b[7], b[8]});
-            if constexpr (QT == 4) s.as[c][row] = __builtin_bit_cast(float, b[9]);
-        }
-    }
     if constexpr (QT == 4) {
         // nibble group `part` -> chunks 2part (low nibbles), 2part+1 (high)
         const u32x4 w0 = r.q[0], w1 = r.q[1];
@@ -279,18 +320,20 @@ struct ChunkD {                      // MFMA results of one chunk
 
 struct Lane {
     int ta, hh, wt, jb, l16;
+    int tx;    // token row whose activation scale this lane broadcasts: 32*wt + mfma_row(l16, hh)
+    int pa0, pa1;  // q6_K: byte offsets in a chunk plane of the two sub-block operands (one is the zero row)
+    int xs[NCH];   // ad_slot(tx, c)
+    int ms[NCH / 2];   // ad_slot(ta, 2k + hh): ssum slot for the min term of chunks 2k, 2k+1
 };
 
 template <int QT>
 __device__ __forceinline__ void load_ab(Ab<QT> &o, const Stage<QT> &s, int c, const Lane &L)
 {
-    const i32x4 av = *reinterpret_cast<const i32x4 *>(&s.a[c][L.ta][16 * (L.hh ^ swz(L.ta))]);
     if constexpr (QT == 4) {
-        o.a0 = av;
+        o.a0 = *reinterpret_cast<const i32x4 *>(&s.a[c][L.ta][16 * (L.hh ^ swz(L.ta))]);
     } else {
-        const i32x4 zero = {0, 0, 0, 0};
-        o.a0 = L.hh ? zero : av;     // first 16 elements of the chunk
-        o.a1 = L.hh ? av : zero;     // last 16
+        o.a0 = *reinterpret_cast<const i32x4 *>(&s.a[c][0][0] + L.pa0);   // first 16 elements
+        o.a1 = *reinterpret_cast<const i32x4 *>(&s.a[c][0][0] + L.pa1);   // last 16
     }
     o.b = *reinterpret_cast<const i32x4 *>(&s.b[c][L.jb][16 * (L.hh ^ swz(L.jb))]);
 }
@@ -298,13 +341,13 @@ __device__ __forceinline__ void load_ab(Ab<QT> &o, const Stage<QT> &s, int c, co
 template <int QT>
 __device__ __forceinline__ void load_sc(Sc<QT> &o, const Stage<QT> &s, int c, const Lane &L)
 {
-    o.x = s.ad[c][32 * L.wt + 16 * L.hh + L.l16];
+    o.x = h2f(s.ad[L.tx][L.xs[c]]);
+    asm volatile("s_nop 1" : "+v"(o.x));     // see fmac_bcast
     if constexpr (QT == 4) {
         o.w0 = s.bs[c][L.jb];
         if (c & 1) {                 // min term of chunks c-1, c: k = lane half
-            const int ck = c - 1 + L.hh;
-            o.am = -s.as[ck][L.ta];
-            o.bm = s.bm[ck][L.jb];
+            o.am = -s.as[L.ta][L.ms[c >> 1]];
+            o.bm = s.bm[c - 1 + L.hh][L.jb];
         }
     } else {
         o.w0 = s.bs[c][L.jb][0];
@@ -324,18 +367,15 @@ __device__ __forceinline__ ChunkD<QT> mfma_chunk(const Ab<QT> &o, const i32x16 &
 // acc += bcast_i(x) * u, where bcast_i hands every lane of a 16-lane row the
 // value x holds in lane i of that row (DPP row_newbcast).  A lane loads the
 // scale of token row mfma_row(lane % 16, lane / 32), so register i of every
-// lane sees the scale of its own row mfma_row(i, lane / 32).  The DPP source
-// x comes straight from an LDS load; the leading s_nop covers the DPP
-// read-after-VALU-write window should x ever be produced by a VALU move.
+// lane sees the scale of its own row mfma_row(i, lane / 32).  A DPP read of a
+// VGPR needs two wait states after a VALU write of it; the compiler cannot see
+// the DPP inside the asm, so x is converted and pinned when it is loaded, two
+// chunks before its first use (load_sc), and never written near a broadcast.
 template <int I>
 __device__ __forceinline__ float fmac_bcast(float acc, float x, float u)
 {
-    if constexpr (I == 0)
-        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf"
-            : "+v"(acc) : "v"(x), "v"(u));
-    else
-        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-            : "+v"(acc) : "v"(x), "v"(u), "i"(I));
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc) : "v"(x), "v"(u), "i"(I));
     return acc;
 }
 
@@ -343,7 +383,14 @@ template <int... I>
 __device__ __forceinline__ void scale_rows(f32x16 &acc, const i32x16 &D, float w, float nw, float x,
                                            std::integer_sequence<int, I...>)
 {
-    ((acc[I] = fmac_bcast<I>(acc[I], x, __builtin_fmaf(as_float(D[I]), w, nw))), ...);
+    // All sixteen products first, each in its own register (the pin keeps the
+    // compiler from pairing every product with its broadcast fma through one
+    // scratch register, which would make the 32 instructions one serial
+    // dependency chain); each broadcast fma then finds its operand long done.
+    f32x16 u;
+    ((u[I] = __builtin_fmaf(as_float(D[I]), w, nw)), ...);
+    pin(u);
+    ((acc[I] = fmac_bcast<I>(acc[I], x, u[I])), ...);
 }
 
 template <int QT, int MODE>
@@ -398,6 +445,16 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     L.ta = 32 * L.wt + (lane & 31);        // token (tile-local) this lane feeds to MFMA a
     L.jb = 32 * (wave >> 1) + (lane & 31); // weight row (tile-local) of the lane
     L.l16 = lane & 15;
+    L.tx = 32 * L.wt + mfma_row(L.l16, L.hh);
+    {
+        const int own = 32 * L.ta + 16 * (L.hh ^ swz(L.ta)), zrow = 32 * TT;
+        L.pa0 = L.hh ? zrow : own;
+        L.pa1 = L.hh ? own : zrow;
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) L.xs[c] = ad_slot(L.tx, c);
+#pragma unroll
+    for (int k = 0; k < NCH / 2; ++k) L.ms[k] = ad_slot(L.ta, 2 * k + L.hh);
     const int64_t j = jw0 + L.jb;
 
     i32x16 bias;
@@ -411,15 +468,27 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     }
 
     const Src src = make_src<QT, WEXP>(g, tw0, jw0);
+    if constexpr (QT == 6) {
+        // the zero rows of both stages (2 x 8 x 32 bytes)
+        if (threadIdx.x < 32) {
+            const int k = threadIdx.x;
+            *reinterpret_cast<u32x4 *>(&st[k >> 4].a[(k >> 1) & 7][TT][16 * (k & 1)]) = u32x4{0, 0, 0, 0};
+        }
+    }
     Raw<QT, WEXP> rw;
+    load_act(st[0], src, 0);
     load_raw(rw, src, 0);
     store_raw(st[0], rw);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the activation copy has landed
     __syncthreads();
 
     for (int64_t sb = 0; sb < nsb; ++sb) {
         const Stage<QT> &s = st[sb & 1];
         const bool more = sb + 1 < nsb;
-        if (more) load_raw(rw, src, sb + 1);
+        if (more) {
+            load_act(st[(sb + 1) & 1], src, sb + 1);
+            load_raw(rw, src, sb + 1);
+        }
 
         // Operand rings, three deep: chunk c+2's MFMA operands and scales are
         // fetched from LDS while chunk c's epilogue runs.
@@ -450,6 +519,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             if constexpr (MODE == 0) pin(acc);                  // epilogue c done here
         }
         if (more) store_raw(st[(sb + 1) & 1], rw);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
