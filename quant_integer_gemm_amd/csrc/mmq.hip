@@ -50,17 +50,29 @@ constexpr int NCH = 8;    // 32-element chunks per super-block
 template <int QT>
 struct Stage;
 
-// Activations arrive by direct global->LDS copies (load_act): the two
-// 16-byte quant halves of every pad40 block, and the d and ssum dwords as
-// they are in the block.  Weights are decoded on the way in (store_raw).
+// Activation quants arrive by direct global->LDS copies (load_act); the
+// activation d and ssum values and the weights go through registers
+// (load_raw / store_raw): d is widened to fp32, ssum and the weights' dmin*m
+// are split into bf16 pairs for the min-term MFMA, the weights are decoded.
+
+// q4_K min term.  -sum_c ssum(t,c) * dmin*m(j,c) is a matrix product with
+// K = 8 per super-block, run on v_mfma_f32_32x32x8_bf16 with both factors
+// split as v = hi + lo (hi = bf16(v), lo = bf16(v - hi)): hi*hi + hi*lo +
+// lo*hi carries v*w to about 2^-16 relative, far inside the output tolerance
+// and at a fraction of the fp32 MFMA's cost.  A MinOp holds the four values
+// of chunks 4h .. 4h+3 of one token or row: hi in dwords 0-1, lo in 2-3, in
+// the element order of the MFMA's K half h.
+struct MinOp {
+    uint32_t w[4];
+};
 template <>
 struct Stage<4> {
     __attribute__((aligned(16))) uint8_t a[NCH][TT][32];   // activation quants (halves swizzled)
-    uint32_t ad[TT][NCH];       // activation block dword 0 (fp16 d in the low half), slot ad_slot
-    float as[TT][NCH];          // activation ssum, same slots
+    float ax[NCH][TT];          // activation d as fp32, token rows in register order (x_slot)
+    MinOp ma[TT][2];            // -ssum of token t, chunks 4h .. 4h+3
     uint8_t b[NCH][TJ][32];     // weight nibbles 0..15 as int8
     float bs[NCH][TJ];          // d * sc
-    float bm[NCH][TJ];          // dmin * m
+    MinOp mb[TJ][2];            // dmin * m of row j, chunks 4h .. 4h+3
 };
 
 // q6_K: row TT of every chunk plane of a is all zero.  Each 16-element
@@ -70,14 +82,15 @@ struct Stage<4> {
 template <>
 struct Stage<6> {
     __attribute__((aligned(16))) uint8_t a[NCH][TT + 1][32];
-    uint32_t ad[TT][NCH];
+    float ax[NCH][TT];
     uint8_t b[NCH][TJ][32];     // centred int8 weights
     float bs[NCH][TJ][2];       // d * sc of the two 16-element sub-blocks
 };
 
-// Chunk c of token t sits in slot c ^ ((t >> 3) & 7) of its ad / as row, so
-// that 32 consecutive tokens reading one chunk hit 32 distinct banks.
-__device__ __forceinline__ int ad_slot(int t, int c) { return c ^ ((t >> 3) & 7); }
+// Position of tile token t in a row of ax: within each 32-token group the
+// tokens are ordered as the rows of the MFMA result registers, so the 16 rows
+// lane half hh holds are 16 consecutive floats (mfma_row(i, hh) -> 16*hh + i).
+__device__ __forceinline__ int x_slot(int t) { return (t & 32) + row_slot(t & 31); }
 
 // The 16-byte half h of row r is stored at half h ^ swz(r).  An LDS access
 // phase serves 8 (32 banks) or 16 (64 banks) lanes reading 16 bytes of
@@ -117,6 +130,15 @@ __device__ __forceinline__ void pin(T &x) { asm volatile("" : "+v"(x)); }
 template <typename T, typename U>
 __device__ __forceinline__ void pin_after(T &x, const U &y) { asm volatile("" : "+v"(x) : "v"(y)); }
 
+// v = hi + lo + O(2^-16 v) with hi, lo bf16 (round to nearest even).
+__device__ __forceinline__ void bf16_split(float v, uint16_t &hi, uint16_t &lo)
+{
+    const __bf16 h = (__bf16)v;
+    const __bf16 l = (__bf16)(v - (float)h);
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, l);
+}
+
 // ---------------------------------------------------------------------------
 // Staging.  Activations are copied straight into LDS (make_src, load_act).
 // Weights go through registers and are decoded on the way into LDS: row =
@@ -136,11 +158,13 @@ struct Raw {
     u32x4 h;       // q4_K header (d, dmin, 12 scale bytes) | q6_K: 16 int8 scales
     u32x4 q[NQ];   // q4_K: 32 nibble bytes | q6_K raw: ql 32 B, qh 32 B | W_exp: 2 x 32 B
     uint32_t d;    // q6_K fp16 d (low half)
+    uint32_t ad[2];   // two activation block dwords (fp16 d in the low half)
+    uint32_t as[2];   // q4_K: ssum of the same two blocks
 };
 
 struct Src {
     const uint8_t *aq[2]; // quant-half source of this lane, token halves 0/1 of the tile
-    const uint8_t *ad[2]; // block source for this lane's d / ssum copies
+    const uint8_t *ad[2]; // blocks of this lane's two activation d (and ssum) loads
     const uint8_t *w;    // weight row start (raw blocks)
     const uint8_t *x;    // W_exp row start (q6_K dense arm)
     int64_t wstep;       // bytes per super-block along w
@@ -157,9 +181,9 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
     // Stage::a (wave w issues q = 4w .. 4w+3) fills a[c][32*th .. +31] with
     // c = q / 2, th = q % 2: lane l brings half h' = l % 2 of token
     // 32*th + l/2, i.e. quant bytes 16*(h' ^ swz(t)) .. +15 of its block.
-    // Dword copy q of ad / as (wave w issues q = 2w, 2w+1) fills tokens
-    // 8q .. 8q+7: lane l fills slot l % 8 of token 8q + l/8, i.e. brings the
-    // block c with ad_slot(t, c) = l % 8 (c = (l % 8) ^ q).
+    // The d (and q4_K ssum) loads of wave w take tokens 8q + l%8 (q = 2w,
+    // 2w+1), chunk l/8: eight tokens of one chunk per lane octet, which keeps
+    // their LDS stores (store_raw) free of conflicts.
     {
         const int l = tid & 63, w = tid >> 6;
 #pragma unroll
@@ -170,9 +194,9 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int t = 8 * (2 * w + i) + (l >> 3);
-            const int64_t tg = min(tw0 + t, g.nt - 1);
-            s.ad[i] = g.q8 + (tg * nb32 + ((l & 7) ^ (t >> 3))) * 40;
+            const int td = 8 * (2 * w + i) + (l & 7);
+            const int64_t tdg = min(tw0 + td, g.nt - 1);
+            s.ad[i] = g.q8 + (tdg * nb32 + (l >> 3)) * 40;
         }
     }
     // Weight staging: lanes l and l+16k of a wave take rows 16w + l%16, so a
@@ -201,20 +225,18 @@ __device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb
         __builtin_amdgcn_global_load_lds((gbl_void_t *)(s.aq[i & 1] + off + 40 * c),
                                          (lds_void_t *)(&st.a[c][32 * (q & 1)][0]), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = 2 * w + i;
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(s.ad[i] + off), (lds_void_t *)(&st.ad[8 * q][0]), 4, 0, 0);
-        if constexpr (QT == 4)
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(s.ad[i] + off + 36), (lds_void_t *)(&st.as[8 * q][0]),
-                                             4, 0, 0);
-    }
 }
 
 template <int QT, bool WEXP>
 __device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t sb)
 {
     const int part = (threadIdx.x >> 4) & 3;
+    r.ad[0] = *reinterpret_cast<const uint32_t *>(s.ad[0] + sb * 320);
+    r.ad[1] = *reinterpret_cast<const uint32_t *>(s.ad[1] + sb * 320);
+    if constexpr (QT == 4) {
+        r.as[0] = *reinterpret_cast<const uint32_t *>(s.ad[0] + sb * 320 + 36);
+        r.as[1] = *reinterpret_cast<const uint32_t *>(s.ad[1] + sb * 320 + 36);
+    }
     const uint8_t *blk = s.w + sb * s.wstep;
     if constexpr (QT == 4) {
         r.h = ld16(blk);
@@ -246,6 +268,19 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
     const int tid = threadIdx.x;
     const int row = 16 * (tid >> 6) + (tid & 15), part = (tid >> 4) & 3;
     const int sw = swz(row);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int l = tid & 63, t = 8 * (2 * (tid >> 6) + i) + (l & 7);
+        s.ax[l >> 3][x_slot(t)] = h2f(r.ad[i]);
+        if constexpr (QT == 4) {
+            const int c = l >> 3;
+            uint16_t hi, lo;
+            bf16_split(-__builtin_bit_cast(float, r.as[i]), hi, lo);
+            uint16_t *m = reinterpret_cast<uint16_t *>(&s.ma[t][c >> 2]);
+            m[c & 3] = hi;
+            m[4 + (c & 3)] = lo;
+        }
+    }
     if constexpr (QT == 4) {
         // nibble group `part` -> chunks 2part (low nibbles), 2part+1 (high)
         const u32x4 w0 = r.q[0], w1 = r.q[1];
@@ -267,7 +302,11 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
             const uint32_t sc = (hi & ((s2 & 15) | ((s0 >> 6) << 4))) | (~hi & (s0 & 63));
             const uint32_t m = (hi & ((s2 >> 4) | ((s1 >> 6) << 4))) | (~hi & (s1 & 63));
             s.bs[b][row] = d * (float)sc;
-            s.bm[b][row] = dmin * (float)m;
+            uint16_t hi, lo;
+            bf16_split(dmin * (float)m, hi, lo);
+            uint16_t *mm = reinterpret_cast<uint16_t *>(&s.mb[row][b >> 2]);
+            mm[b & 3] = hi;
+            mm[4 + (b & 3)] = lo;
         }
     } else {
         const int h = part >> 1, pp = part & 1;
@@ -308,9 +347,7 @@ struct Ab {                          // MFMA operands of one chunk
 
 template <int QT>
 struct Sc {                          // epilogue scales of one chunk
-    float x;                         // activation scale of token row mfma_row(lane % 16, half)
     float w0, w1;                    // weight scale (q6_K: of both sub-blocks)
-    float am, bm;                    // q4_K min-term operands (odd chunks)
 };
 
 template <int QT>
@@ -320,10 +357,7 @@ struct ChunkD {                      // MFMA results of one chunk
 
 struct Lane {
     int ta, hh, wt, jb, l16;
-    int tx;    // token row whose activation scale this lane broadcasts: 32*wt + mfma_row(l16, hh)
     int pa0, pa1;  // q6_K: byte offsets in a chunk plane of the two sub-block operands (one is the zero row)
-    int xs[NCH];   // ad_slot(tx, c)
-    int ms[NCH / 2];   // ad_slot(ta, 2k + hh): ssum slot for the min term of chunks 2k, 2k+1
 };
 
 template <int QT>
@@ -341,14 +375,8 @@ __device__ __forceinline__ void load_ab(Ab<QT> &o, const Stage<QT> &s, int c, co
 template <int QT>
 __device__ __forceinline__ void load_sc(Sc<QT> &o, const Stage<QT> &s, int c, const Lane &L)
 {
-    o.x = h2f(s.ad[L.tx][L.xs[c]]);
-    asm volatile("s_nop 1" : "+v"(o.x));     // see fmac_bcast
     if constexpr (QT == 4) {
         o.w0 = s.bs[c][L.jb];
-        if (c & 1) {                 // min term of chunks c-1, c: k = lane half
-            o.am = -s.as[L.ta][L.ms[c >> 1]];
-            o.bm = s.bm[c - 1 + L.hh][L.jb];
-        }
     } else {
         o.w0 = s.bs[c][L.jb][0];
         o.w1 = s.bs[c][L.jb][1];
@@ -364,44 +392,50 @@ __device__ __forceinline__ ChunkD<QT> mfma_chunk(const Ab<QT> &o, const i32x16 &
     return r;
 }
 
-// acc += bcast_i(x) * u, where bcast_i hands every lane of a 16-lane row the
-// value x holds in lane i of that row (DPP row_newbcast).  A lane loads the
-// scale of token row mfma_row(lane % 16, lane / 32), so register i of every
-// lane sees the scale of its own row mfma_row(i, lane / 32).  A DPP read of a
-// VGPR needs two wait states after a VALU write of it; the compiler cannot see
-// the DPP inside the asm, so x is converted and pinned when it is loaded, two
-// chunks before its first use (load_sc), and never written near a broadcast.
-template <int I>
-__device__ __forceinline__ float fmac_bcast(float acc, float x, float u)
+// The activation scales of the sixteen token rows that this lane's result
+// registers hold, in register order (four 16-byte LDS reads).
+template <int QT>
+__device__ __forceinline__ f32x16 load_x(const Stage<QT> &s, int c, const Lane &L)
 {
-    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc) : "v"(x), "v"(u), "i"(I));
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(&s.ax[c][32 * L.wt + 16 * L.hh]);
+    const f32x4 v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3];
+    return __builtin_shufflevector(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                   __builtin_shufflevector(v2, v3, 0, 1, 2, 3, 4, 5, 6, 7),
+                                   0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+// acc + a * b in the three-operand (VOP3) encoding.  With two waves per SIMD
+// the two-operand v_fmac_f32 form, which the compiler prefers for an
+// accumulation, issues markedly slower on gfx950.
+__device__ __forceinline__ float fma3(float a, float b, float acc)
+{
+    asm("v_fma_f32 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
     return acc;
 }
 
 template <int... I>
-__device__ __forceinline__ void scale_rows(f32x16 &acc, const i32x16 &D, float w, float nw, float x,
+__device__ __forceinline__ void scale_rows(f32x16 &acc, const i32x16 &D, float w, float nw, const f32x16 &x,
                                            std::integer_sequence<int, I...>)
 {
     // All sixteen products first, each in its own register (the pin keeps the
-    // compiler from pairing every product with its broadcast fma through one
+    // compiler from pairing every product with its accumulation through one
     // scratch register, which would make the 32 instructions one serial
-    // dependency chain); each broadcast fma then finds its operand long done.
+    // dependency chain); each accumulation then finds its operand long done.
     f32x16 u;
     ((u[I] = __builtin_fmaf(as_float(D[I]), w, nw)), ...);
     pin(u);
-    ((acc[I] = fmac_bcast<I>(acc[I], x, u[I])), ...);
+    ((acc[I] = fma3(u[I], x[I], acc[I])), ...);
 }
 
 template <int QT, int MODE>
-__device__ __forceinline__ void epilogue(const ChunkD<QT> &D, const Sc<QT> &o, f32x16 &acc,
+__device__ __forceinline__ void epilogue(const ChunkD<QT> &D, const Sc<QT> &o, const f32x16 &x, f32x16 &acc,
                                          const MmqArgs &g, int64_t tw0, int64_t j, int64_t sb, int c,
                                          const Lane &L)
 {
     if constexpr (MODE == 0) {
         constexpr auto rows = std::make_integer_sequence<int, 16>{};
-        scale_rows(acc, D.v[0], o.w0, -MAGIC_F * o.w0, o.x, rows);
-        if constexpr (QT == 6) scale_rows(acc, D.v[1], o.w1, -MAGIC_F * o.w1, o.x, rows);
+        scale_rows(acc, D.v[0], o.w0, -MAGIC_F * o.w0, x, rows);
+        if constexpr (QT == 6) scale_rows(acc, D.v[1], o.w1, -MAGIC_F * o.w1, x, rows);
     } else {
         const int64_t nsb = g.id / 256;
         const int64_t nsub = (QT == 4 ? 8 : 16) * nsb;
@@ -445,16 +479,11 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     L.ta = 32 * L.wt + (lane & 31);        // token (tile-local) this lane feeds to MFMA a
     L.jb = 32 * (wave >> 1) + (lane & 31); // weight row (tile-local) of the lane
     L.l16 = lane & 15;
-    L.tx = 32 * L.wt + mfma_row(L.l16, L.hh);
     {
         const int own = 32 * L.ta + 16 * (L.hh ^ swz(L.ta)), zrow = 32 * TT;
         L.pa0 = L.hh ? zrow : own;
         L.pa1 = L.hh ? own : zrow;
     }
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) L.xs[c] = ad_slot(L.tx, c);
-#pragma unroll
-    for (int k = 0; k < NCH / 2; ++k) L.ms[k] = ad_slot(L.ta, 2 * k + L.hh);
     const int64_t j = jw0 + L.jb;
 
     i32x16 bias;
@@ -494,9 +523,16 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
         // fetched from LDS while chunk c's epilogue runs.
         Ab<QT> ab[3];
         Sc<QT> sc[3];
+        f32x16 xr[2];      // activation scales, loaded one chunk ahead
         ChunkD<QT> dd[2];
         load_ab(ab[0], s, 0, L);
         load_sc(sc[0], s, 0, L);
+        xr[0] = load_x(s, 0, L);
+        MinOp mA, mB;
+        if constexpr (QT == 4 && MODE == 0) {
+            mA = s.ma[L.ta][L.hh];
+            mB = s.mb[L.jb][L.hh];
+        }
         load_ab(ab[1], s, 1, L);
         load_sc(sc[1], s, 1, L);
         dd[0] = mfma_chunk(ab[0], bias);
@@ -506,6 +542,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
                 load_ab(ab[(c + 2) % 3], s, c + 2, L);
                 load_sc(sc[(c + 2) % 3], s, c + 2, L);
             }
+            if (c + 1 < NCH) xr[(c + 1) & 1] = load_x(s, c + 1, L);
             ChunkD<QT> &cur = dd[c & 1];
             if (c + 1 < NCH) {
                 ChunkD<QT> &nxt = dd[(c + 1) & 1];
@@ -513,9 +550,13 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
                 pin_after(cur.v[0], nxt.v[QT == 4 ? 0 : 1]);   // issue MFMA c+1 first
                 if constexpr (QT == 6) pin(cur.v[1]);
             }
-            epilogue<QT, MODE>(cur, sc[c % 3], acc, g, tw0, j, sb, c, L);
-            if constexpr (QT == 4 && MODE == 0)
-                if (c & 1) accm = mfma_f32(sc[c % 3].am, sc[c % 3].bm, accm);
+            epilogue<QT, MODE>(cur, sc[c % 3], xr[c & 1], acc, g, tw0, j, sb, c, L);
+            if constexpr (QT == 4 && MODE == 0) {
+                // the super-block's min term: hi*hi, hi*lo, lo*hi
+                if (c == 2) accm = mfma_bf16(mA.w[0], mA.w[1], mB.w[0], mB.w[1], accm);
+                if (c == 4) accm = mfma_bf16(mA.w[0], mA.w[1], mB.w[2], mB.w[3], accm);
+                if (c == 6) accm = mfma_bf16(mA.w[2], mA.w[3], mB.w[0], mB.w[1], accm);
+            }
             if constexpr (MODE == 0) pin(acc);                  // epilogue c done here
         }
         if (more) store_raw(st[(sb + 1) & 1], rw);

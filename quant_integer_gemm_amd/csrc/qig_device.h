@@ -19,6 +19,7 @@ namespace qig {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Starting an int32 MFMA accumulator at the bit pattern of 1.5*2^23 makes the
@@ -36,6 +37,16 @@ __device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c)
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 32x32x8 bf16 -> fp32; each operand is four bf16 packed in two dwords.
+__device__ __forceinline__ f32x16 mfma_bf16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x16 c)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const s16x4 a = __builtin_bit_cast(s16x4, u32x2{a0, a1});
+    const s16x4 b = __builtin_bit_cast(s16x4, u32x2{b0, b1});
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Reinterpret an int32 as fp32.  Takes the value by copy: clang's
