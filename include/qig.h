@@ -76,8 +76,10 @@ int quantize_q8_pad40(const float *x, int64_t nt, int64_t id, int64_t ldx,
  *   q8     pad40 plane of nt tokens x id, 16-byte aligned
  *   y      [nt][ldy] fp32, ldy >= od; overwritten (not accumulated),
  *          4-byte aligned
- * Errors: QIG_EINVAL (nt < 0, od < 0, id <= 0 or id % 256, ldy < od),
- *         QIG_EALIGN, QIG_ELAUNCH.
+ * Errors: QIG_EINVAL (nt < 0, od < 0, id <= 0 or id % 256, ldy < od, or
+ *         id too large for 32-bit offsets within one 64-token, 64-row tile:
+ *         80*id, id*bstride/4 (bstride = 144 here) and 64*id must stay below
+ *         2^31), QIG_EALIGN, QIG_ELAUNCH.
  */
 int mmq_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt,
             float *y, int64_t ldy, hipStream_t stream);

@@ -10,10 +10,20 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int rc_from_launch(int r) { return r == 0 ? QIG_OK : (r == -1 ? QIG_EINVAL : QIG_ELAUNCH); }
 
+// The GEMM kernels address the bytes of one 64-token, 64-row tile with
+// 32-bit offsets: 64 pad40 rows (80 * id bytes), 64 raw weight rows
+// (id * bstride / 4) and 64 dense-plane rows (64 * id).
+bool tile_span_ok(int64_t id, int64_t bstride)
+{
+    const int64_t lim = int64_t(1) << 31;
+    return id < lim / 80 && id / 4 < lim / bstride && id < lim / 64;
+}
+
 int check_gemm(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, const void *out,
-               int64_t ldy)
+               int64_t ldy, int64_t bstride)
 {
     if (nt < 0 || od < 0 || id <= 0 || id % 256 != 0) return QIG_EINVAL;
+    if (!tile_span_ok(id, bstride)) return QIG_EINVAL;
     if (ldy < od) return QIG_EINVAL;
     if (nt == 0 || od == 0) return QIG_OK;
     if (!W || !q8 || !out) return QIG_EINVAL;
@@ -61,7 +71,7 @@ int quantize_q8_pad40(const float *x, int64_t nt, int64_t id, int64_t ldx, void 
 int mmq_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
             hipStream_t stream)
 {
-    int rc = check_gemm(W, od, id, q8, nt, y, ldy);
+    int rc = check_gemm(W, od, id, q8, nt, y, ldy, 144);
     if (rc != QIG_OK || nt == 0 || od == 0) return rc;
     qig::MmqLaunch L = {4, W, nullptr, q8, y, nullptr, 144, od, id, nt, ldy, 0, nt, 0, od};
     return rc_from_launch(qig::launch_mmq(L, stream));
@@ -71,7 +81,7 @@ int mmq_q6k(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int
             int64_t nt, float *y, int64_t ldy, hipStream_t stream)
 {
     if (bad_bstride(bstride)) return QIG_EINVAL;
-    int rc = check_gemm(W, od, id, q8, nt, y, ldy);
+    int rc = check_gemm(W, od, id, q8, nt, y, ldy, bstride);
     if (rc != QIG_OK || nt == 0 || od == 0) return rc;
     if (W_exp && !aligned(W_exp, 16)) return QIG_EALIGN;
     qig::MmqLaunch L = {6, W, W_exp, q8, y, nullptr, bstride, od, id, nt, ldy, 0, nt, 0, od};
@@ -91,7 +101,7 @@ int expand_q6k_dense(const void *W, int64_t bstride, int64_t od, int64_t id, int
 int mmq_q4k_partials(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, int64_t t0,
                      int64_t t1, int64_t j0, int64_t j1, int32_t *P, hipStream_t stream)
 {
-    int rc = check_gemm(W, od, id, q8, nt, P, od);
+    int rc = check_gemm(W, od, id, q8, nt, P, od, 144);
     if (rc != QIG_OK) return rc;
     if (bad_window(nt, od, t0, t1, j0, j1)) return QIG_EINVAL;
     if (t1 == t0 || j1 == j0) return QIG_OK;
@@ -104,7 +114,7 @@ int mmq_q6k_partials(const void *W, int64_t bstride, const int8_t *W_exp, int64_
                      hipStream_t stream)
 {
     if (bad_bstride(bstride)) return QIG_EINVAL;
-    int rc = check_gemm(W, od, id, q8, nt, P, od);
+    int rc = check_gemm(W, od, id, q8, nt, P, od, bstride);
     if (rc != QIG_OK) return rc;
     if (W_exp && !aligned(W_exp, 16)) return QIG_EALIGN;
     if (bad_window(nt, od, t0, t1, j0, j1)) return QIG_EINVAL;

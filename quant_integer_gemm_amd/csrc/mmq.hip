@@ -162,11 +162,19 @@ struct Raw {
     uint32_t as[2];   // q4_K: ssum of the same two blocks
 };
 
+// Staging sources: workgroup-uniform bases (the tile's first token / row, so
+// they live in scalar registers and advance per super-block with scalar
+// adds) plus 32-bit per-lane byte offsets, which the loads take as their
+// vector offset.  A tile spans 64 tokens and 64 rows, so every offset is
+// below 64 * (id / 32) * 40 or 64 * (id / 256) * bstride.
 struct Src {
-    const uint8_t *aq[2]; // quant-half source of this lane, token halves 0/1 of the tile
-    const uint8_t *ad[2]; // blocks of this lane's two activation d (and ssum) loads
-    const uint8_t *w;    // weight row start (raw blocks)
-    const uint8_t *x;    // W_exp row start (q6_K dense arm)
+    const uint8_t *q8;   // pad40 plane at the tile's first token
+    const uint8_t *w;    // raw weight rows at the tile's first row
+    const uint8_t *x;    // W_exp rows at the tile's first row (q6_K dense arm)
+    uint32_t aq[2];      // this lane's quant-half sources, token halves 0/1 of the tile
+    uint32_t ad[2];      // blocks of this lane's two activation d (and ssum) loads
+    uint32_t wo;         // this lane's weight row
+    uint32_t xo;         // this lane's W_exp row
     int64_t wstep;       // bytes per super-block along w
 };
 
@@ -184,27 +192,31 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
     // The d (and q4_K ssum) loads of wave w take tokens 8q + l%8 (q = 2w,
     // 2w+1), chunk l/8: eight tokens of one chunk per lane octet, which keeps
     // their LDS stores (store_raw) free of conflicts.
+    const uint32_t tok = (uint32_t)(nb32 * 40);      // bytes per token
+    s.q8 = g.q8 + tw0 * (int64_t)tok;
     {
         const int l = tid & 63, w = tid >> 6;
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
             const int t = 32 * th + (l >> 1);
-            const int64_t tg = min(tw0 + t, g.nt - 1);
-            s.aq[th] = g.q8 + tg * nb32 * 40 + 4 + 16 * ((l & 1) ^ swz(t));
+            const uint32_t tl = (uint32_t)(min(tw0 + t, g.nt - 1) - tw0);
+            s.aq[th] = tl * tok + 4 + 16 * ((l & 1) ^ swz(t));
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int td = 8 * (2 * w + i) + (l & 7);
-            const int64_t tdg = min(tw0 + td, g.nt - 1);
-            s.ad[i] = g.q8 + (tdg * nb32 + (l >> 3)) * 40;
+            const uint32_t tl = (uint32_t)(min(tw0 + td, g.nt - 1) - tw0);
+            s.ad[i] = tl * tok + (l >> 3) * 40;
         }
     }
     // Weight staging: lanes l and l+16k of a wave take rows 16w + l%16, so a
     // load covers 16 rows (not 64) and the LDS writes stay conflict free.
-    const int64_t j = min(jw0 + 16 * (tid >> 6) + (tid & 15), g.od - 1);
+    const uint32_t jl = (uint32_t)(min(jw0 + 16 * (tid >> 6) + (tid & 15), g.od - 1) - jw0);
     s.wstep = QT == 4 ? 144 : g.bstride;
-    s.w = g.W + j * nsb * s.wstep;
-    s.x = WEXP ? g.Wexp + j * g.id : nullptr;
+    s.w = g.W + jw0 * nsb * s.wstep;
+    s.wo = jl * (uint32_t)(nsb * s.wstep);
+    s.x = WEXP ? g.Wexp + jw0 * g.id : nullptr;
+    s.xo = jl * (uint32_t)g.id;
     return s;
 }
 
@@ -217,12 +229,12 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 template <int QT>
 __device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb)
 {
-    const int w = threadIdx.x >> 6;
-    const int64_t off = sb * 320;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const uint8_t *q8 = s.q8 + sb * 320;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = 4 * w + i, c = q >> 1;
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(s.aq[i & 1] + off + 40 * c),
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(q8 + 40 * c + s.aq[i & 1]),
                                          (lds_void_t *)(&st.a[c][32 * (q & 1)][0]), 16, 0, 0);
     }
 }
@@ -231,13 +243,14 @@ template <int QT, bool WEXP>
 __device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t sb)
 {
     const int part = (threadIdx.x >> 4) & 3;
-    r.ad[0] = *reinterpret_cast<const uint32_t *>(s.ad[0] + sb * 320);
-    r.ad[1] = *reinterpret_cast<const uint32_t *>(s.ad[1] + sb * 320);
+    const uint8_t *q8 = s.q8 + sb * 320;
+    r.ad[0] = *reinterpret_cast<const uint32_t *>(q8 + s.ad[0]);
+    r.ad[1] = *reinterpret_cast<const uint32_t *>(q8 + s.ad[1]);
     if constexpr (QT == 4) {
-        r.as[0] = *reinterpret_cast<const uint32_t *>(s.ad[0] + sb * 320 + 36);
-        r.as[1] = *reinterpret_cast<const uint32_t *>(s.ad[1] + sb * 320 + 36);
+        r.as[0] = *reinterpret_cast<const uint32_t *>(q8 + 36 + s.ad[0]);
+        r.as[1] = *reinterpret_cast<const uint32_t *>(q8 + 36 + s.ad[1]);
     }
-    const uint8_t *blk = s.w + sb * s.wstep;
+    const uint8_t *blk = s.w + sb * s.wstep + s.wo;
     if constexpr (QT == 4) {
         r.h = ld16(blk);
         r.q[0] = ld16(blk + 16 + 32 * part);
@@ -246,7 +259,7 @@ __device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t
         const int h = part >> 1, pp = part & 1;
         if constexpr (WEXP) {
             // chunks 4h+pp and 4h+pp+2 of the dense plane
-            const uint8_t *px = s.x + sb * 256 + 128 * h + 32 * pp;
+            const uint8_t *px = s.x + sb * 256 + s.xo + 128 * h + 32 * pp;
             r.q[0] = ld16(px);
             r.q[1] = ld16(px + 16);
             r.q[2] = ld16(px + 64);
@@ -288,26 +301,26 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
         st16(&s.b[2 * part][row][16 * (1 ^ sw)], w1 & 0x0F0F0F0Fu);
         st16(&s.b[2 * part + 1][row][16 * (0 ^ sw)], (w0 >> 4) & 0x0F0F0F0Fu);
         st16(&s.b[2 * part + 1][row][16 * (1 ^ sw)], (w1 >> 4) & 0x0F0F0F0Fu);
-        // scale/min of sub-blocks 2part, 2part+1 from the twelve packed bytes
-        // S[0..11] = header bytes 4..15.
+        // scale/min of sub-blocks part (< 4) and part + 4 from the twelve
+        // packed bytes S[0..11] = header bytes 4..15: byte `part` of each of
+        // the three scale dwords.
         const float d = h2f(r.h[0]), dmin = h2f(r.h[0] >> 16);
-        const uint32_t hi = part >= 2 ? 0xffffffffu : 0u;    // sub-blocks 4..7
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int b = 2 * part + k;
-            const int sh = 8 * (b & 3);                         // byte (b mod 4) of each group
-            const uint32_t s0 = (r.h[1] >> sh) & 0xff;          // S[b mod 4]
-            const uint32_t s1 = (r.h[2] >> sh) & 0xff;          // S[4 + b mod 4]
-            const uint32_t s2 = (r.h[3] >> sh) & 0xff;          // S[8 + b mod 4]
-            const uint32_t sc = (hi & ((s2 & 15) | ((s0 >> 6) << 4))) | (~hi & (s0 & 63));
-            const uint32_t m = (hi & ((s2 >> 4) | ((s1 >> 6) << 4))) | (~hi & (s1 & 63));
-            s.bs[b][row] = d * (float)sc;
-            uint16_t hi, lo;
-            bf16_split(dmin * (float)m, hi, lo);
-            uint16_t *mm = reinterpret_cast<uint16_t *>(&s.mb[row][b >> 2]);
-            mm[b & 3] = hi;
-            mm[4 + (b & 3)] = lo;
-        }
+        const uint32_t s0 = __builtin_amdgcn_ubfe(r.h[1], 8 * part, 8);   // S[part]
+        const uint32_t s1 = __builtin_amdgcn_ubfe(r.h[2], 8 * part, 8);   // S[part + 4]
+        const uint32_t s2 = __builtin_amdgcn_ubfe(r.h[3], 8 * part, 8);   // S[part + 8]
+        const uint32_t sc0 = s0 & 63, m0 = s1 & 63;
+        const uint32_t sc1 = (s2 & 15) | ((s0 >> 2) & 0x30), m1 = (s2 >> 4) | ((s1 >> 2) & 0x30);
+        s.bs[part][row] = d * (float)sc0;
+        s.bs[part + 4][row] = d * (float)sc1;
+        uint16_t hi, lo;
+        uint16_t *mm0 = reinterpret_cast<uint16_t *>(&s.mb[row][0]);
+        uint16_t *mm1 = reinterpret_cast<uint16_t *>(&s.mb[row][1]);
+        bf16_split(dmin * (float)m0, hi, lo);
+        mm0[part] = hi;
+        mm0[4 + part] = lo;
+        bf16_split(dmin * (float)m1, hi, lo);
+        mm1[part] = hi;
+        mm1[4 + part] = lo;
     } else {
         const int h = part >> 1, pp = part & 1;
 #pragma unroll
@@ -319,11 +332,17 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
                 o[0] = r.q[2 * z];
                 o[1] = r.q[2 * z + 1];
             } else {
+                // quarter qq: nibble z of ql, bits 2qq..2qq+1 of qh moved to 4..5
+                const int lsh = 4 - 2 * pp;    // z = 0: qh << (4 - 2pp); z = 1: qh >> 2pp
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)   // output dword 4h2+e of the chunk
-                        o[h2][e] = q6_centred(r.q[h2][e], r.q[2 + h2][e], qq);
+                    for (int e = 0; e < 4; ++e) {   // output dword 4h2+e of the chunk
+                        const uint32_t ql = r.q[h2][e], qh = r.q[2 + h2][e];
+                        const uint32_t nib = z == 0 ? (ql & 0x0F0F0F0Fu) : ((ql >> 4) & 0x0F0F0F0Fu);
+                        const uint32_t hi2 = (z == 0 ? (qh << lsh) : (qh >> (2 * pp))) & 0x30303030u;
+                        o[h2][e] = q6_centre(nib + hi2);
+                    }
             }
             st16(&s.b[c][row][16 * (0 ^ sw)], o[0]);
             st16(&s.b[c][row][16 * (1 ^ sw)], o[1]);

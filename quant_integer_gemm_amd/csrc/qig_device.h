@@ -75,16 +75,22 @@ __device__ __forceinline__ int row_slot(int tau)
     return 16 * ((tau >> 2) & 1) + 4 * (tau >> 3) + (tau & 3);
 }
 
+// Four 6-bit values v in [0, 63], one per byte, to the two's-complement
+// bytes of v - 32: v + 0x60 stays below 0x100 (no carry between bytes) and
+// flipping bit 7 then gives v - 32 modulo 256.
+__device__ __forceinline__ uint32_t q6_centre(uint32_t v)
+{
+    return (v + 0x60606060u) ^ 0x80808080u;
+}
+
 // q6_K: four centred int8 weights from one ql dword and one qh dword.
 // quarter qq (0..3) picks the nibble (low for 0,1; high for 2,3) and the
-// 2-bit field of qh.  Bytes are in [0, 63] before centring; OR-ing 0x80 keeps
-// the per-byte subtraction of 32 from borrowing across bytes, XOR 0x80 then
-// gives the two's-complement value - 32.
+// 2-bit field of qh, which lands in bits 4-5 of each byte.
 __device__ __forceinline__ uint32_t q6_centred(uint32_t qlw, uint32_t qhw, int qq)
 {
-    uint32_t nib = (qq < 2) ? (qlw & 0x0F0F0F0Fu) : ((qlw >> 4) & 0x0F0F0F0Fu);
-    uint32_t hi2 = ((qhw >> (2 * qq)) & 0x03030303u) << 4;
-    return ((nib | hi2 | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+    const uint32_t nib = (qq < 2) ? (qlw & 0x0F0F0F0Fu) : ((qlw >> 4) & 0x0F0F0F0Fu);
+    const uint32_t hi2 = ((qhw >> (2 * qq)) << 4) & 0x30303030u;
+    return q6_centre(nib + hi2);
 }
 
 // q4_K 6-bit scale and min of sub-block b from the twelve packed bytes S.

@@ -84,6 +84,8 @@ def test_mmq_q4k_argument_checks(args, rc):
     ((A16, 216, None, 8, 256, B16, 4, A16, 8, None), -1),   # bstride % 16
     ((A16, 224, MIS, 8, 256, B16, 4, A16, 8, None), -2),    # W_exp misaligned
     ((A16, 224, None, 8, 512, B16, 0, A16, 8, None), 0),
+    ((A16, 224, None, 8, 1 << 25, B16, 4, A16, 8, None), -1),      # tile span beyond 32-bit offsets
+    ((A16, 1 << 20, None, 8, 1 << 14, B16, 4, A16, 8, None), -1),  # id * bstride / 4 >= 2^31
 ])
 def test_mmq_q6k_argument_checks(args, rc):
     assert qig.load().mmq_q6k(*args) == rc
