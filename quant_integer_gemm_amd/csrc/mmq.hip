@@ -154,9 +154,9 @@ __device__ __forceinline__ void bf16_split(float v, uint16_t &hi, uint16_t &lo)
 // ---------------------------------------------------------------------------
 template <int QT, bool WEXP>
 struct Raw {
-    static constexpr int NQ = QT == 4 ? 2 : 4;
+    static constexpr int NQ = QT == 4 ? 2 : (WEXP ? 1 : 4);
     u32x4 h;       // q4_K header (d, dmin, 12 scale bytes) | q6_K: 16 int8 scales
-    u32x4 q[NQ];   // q4_K: 32 nibble bytes | q6_K raw: ql 32 B, qh 32 B | W_exp: 2 x 32 B
+    u32x4 q[NQ];   // q4_K: 32 nibble bytes | q6_K raw: ql 32 B, qh 32 B | W_exp: unused
     uint32_t d;    // q6_K fp16 d (low half)
     uint32_t ad[2];   // two activation block dwords (fp16 d in the low half)
     uint32_t as[2];   // q4_K: ssum of the same two blocks
@@ -174,7 +174,7 @@ struct Src {
     uint32_t aq[2];      // this lane's quant-half sources, token halves 0/1 of the tile
     uint32_t ad[2];      // blocks of this lane's two activation d (and ssum) loads
     uint32_t wo;         // this lane's weight row
-    uint32_t xo;         // this lane's W_exp row
+    uint32_t xq[2];      // this lane's W_exp copy sources, row halves 0/1 of the tile
     int64_t wstep;       // bytes per super-block along w
 };
 
@@ -215,8 +215,18 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
     s.wstep = QT == 4 ? 144 : g.bstride;
     s.w = g.W + jw0 * nsb * s.wstep;
     s.wo = jl * (uint32_t)(nsb * s.wstep);
+    // W_exp copies: the same mapping as the activation quant copies, with
+    // weight rows in place of tokens (a row's chunk is 32 plain bytes).
     s.x = WEXP ? g.Wexp + jw0 * g.id : nullptr;
-    s.xo = jl * (uint32_t)g.id;
+    {
+        const int l = tid & 63;
+#pragma unroll
+        for (int jh = 0; jh < 2; ++jh) {
+            const int r = 32 * jh + (l >> 1);
+            const uint32_t rl = (uint32_t)(min(jw0 + r, g.od - 1) - jw0);
+            s.xq[jh] = rl * (uint32_t)g.id + 16 * ((l & 1) ^ swz(r));
+        }
+    }
     return s;
 }
 
@@ -239,6 +249,20 @@ __device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb
     }
 }
 
+// q6_K dense arm: direct global->LDS copies of super-block sb's quants from
+// W_exp into stage b (same completion rule as load_act).
+__device__ __forceinline__ void load_wexp(Stage<6> &st, const Src &s, int64_t sb)
+{
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const uint8_t *x = s.x + sb * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = 4 * w + i, c = q >> 1;
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(x + 32 * c + s.xq[i & 1]),
+                                         (lds_void_t *)(&st.b[c][32 * (q & 1)][0]), 16, 0, 0);
+    }
+}
+
 template <int QT, bool WEXP>
 __device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t sb)
 {
@@ -257,14 +281,7 @@ __device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t
         r.q[1] = ld16(blk + 32 + 32 * part);
     } else {
         const int h = part >> 1, pp = part & 1;
-        if constexpr (WEXP) {
-            // chunks 4h+pp and 4h+pp+2 of the dense plane
-            const uint8_t *px = s.x + sb * 256 + s.xo + 128 * h + 32 * pp;
-            r.q[0] = ld16(px);
-            r.q[1] = ld16(px + 16);
-            r.q[2] = ld16(px + 64);
-            r.q[3] = ld16(px + 80);
-        } else {
+        if constexpr (!WEXP) {
             r.q[0] = ld16(blk + 64 * h + 32 * pp);        // ql bytes of quarters pp, pp+2
             r.q[1] = ld16(blk + 64 * h + 32 * pp + 16);
             r.q[2] = ld16(blk + 128 + 32 * h);            // qh bytes of this half
@@ -327,11 +344,8 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
         for (int z = 0; z < 2; ++z) {
             const int qq = pp + 2 * z;          // quarter of the half
             const int c = 4 * h + qq;
-            u32x4 o[2];
-            if constexpr (WEXP) {
-                o[0] = r.q[2 * z];
-                o[1] = r.q[2 * z + 1];
-            } else {
+            if constexpr (!WEXP) {
+                u32x4 o[2];
                 // quarter qq: nibble z of ql, bits 2qq..2qq+1 of qh moved to 4..5
                 const int lsh = 4 - 2 * pp;    // z = 0: qh << (4 - 2pp); z = 1: qh >> 2pp
 #pragma unroll
@@ -343,9 +357,9 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
                         const uint32_t hi2 = (z == 0 ? (qh << lsh) : (qh >> (2 * pp))) & 0x30303030u;
                         o[h2][e] = q6_centre(nib + hi2);
                     }
+                st16(&s.b[c][row][16 * (0 ^ sw)], o[0]);
+                st16(&s.b[c][row][16 * (1 ^ sw)], o[1]);
             }
-            st16(&s.b[c][row][16 * (0 ^ sw)], o[0]);
-            st16(&s.b[c][row][16 * (1 ^ sw)], o[1]);
             const uint32_t v = r.h[c >> 1];             // scale bytes 2c, 2c+1
             const int sh = 16 * (c & 1);
             const float d = h2f(r.d);
@@ -525,6 +539,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     }
     Raw<QT, WEXP> rw;
     load_act(st[0], src, 0);
+    if constexpr (WEXP) load_wexp(st[0], src, 0);
     load_raw(rw, src, 0);
     store_raw(st[0], rw);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the activation copy has landed
@@ -535,6 +550,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
         const bool more = sb + 1 < nsb;
         if (more) {
             load_act(st[(sb + 1) & 1], src, sb + 1);
+            if constexpr (WEXP) load_wexp(st[(sb + 1) & 1], src, sb + 1);
             load_raw(rw, src, sb + 1);
         }
 
