@@ -124,6 +124,43 @@ int expand_q6k_dense(const void *W, int64_t bstride, int64_t od, int64_t id,
                      int8_t *W_exp, hipStream_t stream);
 
 /*
+ * Prepared weights -- registration-time planes that let the GEMM stage its
+ * weights without decoding them (device memory traded for work, as the
+ * dense-plane arm above does for q6_K quants; r44 page s2.4 weighs that
+ * trade).  A prepared buffer of qNk_prepared_bytes(od, id) = Qb +
+ * od*(id/256)*64 bytes holds
+ *   quant plane  at offset 0, Qb bytes.  q6_K: int8 [od][id], the values
+ *                centred to [-32, 31] (the same bytes as expand_q6k_dense),
+ *                Qb = od*id.  q4_K: the packed 4-bit quants of each block
+ *                as in the raw block, [od][id/2] with 128 bytes per
+ *                super-block, Qb = od*id/2 (a byte per element measured
+ *                slower: it doubles the bytes the GEMM loads)
+ *   scale plane  fp32 [od][id/256][16] at offset Qb:
+ *                q4_K: d*sc_b, dmin*m_b for b = 0..7, in pairs;
+ *                q6_K: d*sc of the 16 sub-blocks,
+ * each product formed as the raw-block GEMM forms it (one fp32 rounding of
+ * fp16 d times the integer scale), so mmq_qNk_prepared gives bit-identical y
+ * to mmq_qNk on the raw blocks.  The layout is part of this contract.  The
+ * q6_K buffer removes all weight decoding from the GEMM; the q4_K buffer
+ * removes the 6-bit scale/min unpacking and keeps the nibble split.
+ *
+ *   W     raw blocks as for mmq_q4k / mmq_q6k, 16-byte aligned
+ *   Wp    the prepared buffer, 16-byte aligned; every byte written
+ * qNk_prepared_bytes returns 0 for invalid shapes.  prepare_*: QIG_EINVAL
+ * (od < 0, id <= 0 or id % 256, bad bstride), QIG_EALIGN, QIG_ELAUNCH.
+ * mmq_qNk_prepared: arguments and errors as mmq_q4k with W replaced by Wp.
+ */
+size_t q4k_prepared_bytes(int64_t od, int64_t id);
+size_t q6k_prepared_bytes(int64_t od, int64_t id);
+int prepare_q4k(const void *W, int64_t od, int64_t id, void *Wp, hipStream_t stream);
+int prepare_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, void *Wp,
+                hipStream_t stream);
+int mmq_q4k_prepared(const void *Wp, int64_t od, int64_t id, const void *q8,
+                     int64_t nt, float *y, int64_t ldy, hipStream_t stream);
+int mmq_q6k_prepared(const void *Wp, int64_t od, int64_t id, const void *q8,
+                     int64_t nt, float *y, int64_t ldy, hipStream_t stream);
+
+/*
  * Test exports: the int32 sub-block partials of the same kernels, for the
  * window of tokens [t0, t1) and rows [j0, j1), written to
  * P[(t - t0)][(j - j0)][sub] (int32, 4-byte aligned), where sub runs over all

@@ -29,6 +29,12 @@ SIGNATURES = {
     "mmq_q4k_partials": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
     "mmq_q6k_partials": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
                                         _vp, _vp]),
+    "q4k_prepared_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "q6k_prepared_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "prepare_q4k": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
+    "prepare_q6k": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "mmq_q4k_prepared": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "mmq_q6k_prepared": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
 }
 
 
@@ -149,3 +155,44 @@ def mmq_q6k_partials(W, bstride, od, id_, q8, nt, t0, t1, j0, j1, W_exp=None, st
                                    _dev_ptr(q8, "q8"), nt, t0, t1, j0, j1, _dev_ptr(P, "P"),
                                    _stream(stream)), "mmq_q6k_partials")
     return P
+
+
+def prepared_bytes(qtype: str, od: int, id_: int) -> int:
+    """Size of a prepared buffer: od*id quant bytes + od*(id/256)*64 scale bytes."""
+    fn = load().q4k_prepared_bytes if qtype == "q4_K" else load().q6k_prepared_bytes
+    return int(fn(od, id_))
+
+
+def prepare_q4k(W, od: int, id_: int, out=None, stream=None):
+    """Raw q4_K plane -> prepared buffer (quant plane + fp32 scale plane)."""
+    import torch
+    if out is None:
+        out = torch.empty(prepared_bytes("q4_K", od, id_), dtype=torch.uint8, device=W.device)
+    _check(load().prepare_q4k(_dev_ptr(W, "W"), od, id_, _dev_ptr(out, "Wp"), _stream(stream)), "prepare_q4k")
+    return out
+
+
+def prepare_q6k(W, bstride: int, od: int, id_: int, out=None, stream=None):
+    """Raw q6_K plane -> prepared buffer (quant plane + fp32 scale plane)."""
+    import torch
+    if out is None:
+        out = torch.empty(prepared_bytes("q6_K", od, id_), dtype=torch.uint8, device=W.device)
+    _check(load().prepare_q6k(_dev_ptr(W, "W"), bstride, od, id_, _dev_ptr(out, "Wp"), _stream(stream)),
+           "prepare_q6k")
+    return out
+
+
+def mmq_q4k_prepared(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, stream=None):
+    """y[nt][od] from a prepared q4_K buffer (bit-identical to mmq_q4k on the raw blocks)."""
+    y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    _check(load().mmq_q4k_prepared(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
+                                   _stream(stream)), "mmq_q4k_prepared")
+    return y
+
+
+def mmq_q6k_prepared(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, stream=None):
+    """y[nt][od] from a prepared q6_K buffer (bit-identical to mmq_q6k on the raw blocks)."""
+    y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    _check(load().mmq_q6k_prepared(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
+                                   _stream(stream)), "mmq_q6k_prepared")
+    return y

@@ -98,6 +98,66 @@ int expand_q6k_dense(const void *W, int64_t bstride, int64_t od, int64_t id, int
     return rc_from_launch(qig::launch_expand_q6k(W, bstride, od, id, W_exp, stream));
 }
 
+// quant plane bytes of a prepared buffer: q4_K keeps packed nibbles
+static int64_t prepared_quant_bytes(int qtype, int64_t od, int64_t id) { return qtype == 4 ? od * (id / 2) : od * id; }
+
+static size_t prepared_bytes(int qtype, int64_t od, int64_t id)
+{
+    if (od < 0 || id <= 0 || id % 256 != 0) return 0;
+    return (size_t)prepared_quant_bytes(qtype, od, id) + (size_t)od * (size_t)(id / 256) * 64u;
+}
+
+size_t q4k_prepared_bytes(int64_t od, int64_t id) { return prepared_bytes(4, od, id); }
+
+size_t q6k_prepared_bytes(int64_t od, int64_t id) { return prepared_bytes(6, od, id); }
+
+int prepare_q4k(const void *W, int64_t od, int64_t id, void *Wp, hipStream_t stream)
+{
+    if (od < 0 || id <= 0 || id % 256 != 0) return QIG_EINVAL;
+    if (od == 0) return QIG_OK;
+    if (!W || !Wp) return QIG_EINVAL;
+    if (!aligned(W, 16) || !aligned(Wp, 16)) return QIG_EALIGN;
+    int8_t *Q = static_cast<int8_t *>(Wp);
+    float *S = reinterpret_cast<float *>(static_cast<uint8_t *>(Wp) + prepared_quant_bytes(4, od, id));
+    return rc_from_launch(qig::launch_prepare_q4k(W, od, id, Q, S, stream));
+}
+
+int prepare_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, void *Wp, hipStream_t stream)
+{
+    if (bad_bstride(bstride) || od < 0 || id <= 0 || id % 256 != 0) return QIG_EINVAL;
+    if (od == 0) return QIG_OK;
+    if (!W || !Wp) return QIG_EINVAL;
+    if (!aligned(W, 16) || !aligned(Wp, 16)) return QIG_EALIGN;
+    int8_t *Q = static_cast<int8_t *>(Wp);
+    float *S = reinterpret_cast<float *>(static_cast<uint8_t *>(Wp) + od * id);
+    int rc = rc_from_launch(qig::launch_expand_q6k(W, bstride, od, id, Q, stream));
+    if (rc != QIG_OK) return rc;
+    return rc_from_launch(qig::launch_prepare_q6k_scales(W, bstride, od, id, S, stream));
+}
+
+static int mmq_prepared(int qtype, const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y,
+                        int64_t ldy, hipStream_t stream)
+{
+    int rc = check_gemm(Wp, od, id, q8, nt, y, ldy, 64);
+    if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    const int8_t *Q = static_cast<const int8_t *>(Wp);
+    const void *S = static_cast<const uint8_t *>(Wp) + prepared_quant_bytes(qtype, od, id);
+    qig::MmqLaunch L = {qtype, S, Q, q8, y, nullptr, 64, od, id, nt, ldy, 0, nt, 0, od, true};
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
+int mmq_q4k_prepared(const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
+                     hipStream_t stream)
+{
+    return mmq_prepared(4, Wp, od, id, q8, nt, y, ldy, stream);
+}
+
+int mmq_q6k_prepared(const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
+                     hipStream_t stream)
+{
+    return mmq_prepared(6, Wp, od, id, q8, nt, y, ldy, stream);
+}
+
 int mmq_q4k_partials(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, int64_t t0,
                      int64_t t1, int64_t j0, int64_t j1, int32_t *P, hipStream_t stream)
 {

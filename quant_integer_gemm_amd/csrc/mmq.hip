@@ -46,6 +46,15 @@ constexpr int TT = 64;    // tokens per workgroup tile
 constexpr int TJ = 64;    // weight rows per workgroup tile
 constexpr int NCH = 8;    // 32-element chunks per super-block
 
+// Weight sources ("arms").  RAW: raw blocks, decoded on the way into LDS.
+// WEXP (q6_K): quants from the dense plane W_exp, copied straight into LDS;
+// d and the scales from the raw blocks.  PREP: a prepared buffer made once at
+// registration, with the scales as an fp32 plane loaded as they are; its
+// quants are copied straight into LDS (q6_K, one centred byte per element)
+// or split from packed nibbles as in RAW (q4_K, whose nibble plane moves
+// half the bytes of a byte plane).
+constexpr int ARM_RAW = 0, ARM_WEXP = 1, ARM_PREP = 2;
+
 // One super-block of staged operands.
 template <int QT>
 struct Stage;
@@ -152,11 +161,12 @@ __device__ __forceinline__ void bf16_split(float v, uint16_t &hi, uint16_t &lo)
 // one: the loads stay unconditional and a clamped row only feeds outputs that
 // are never stored.
 // ---------------------------------------------------------------------------
-template <int QT, bool WEXP>
+template <int QT, int ARM>
 struct Raw {
-    static constexpr int NQ = QT == 4 ? 2 : (WEXP ? 1 : 4);
-    u32x4 h;       // q4_K header (d, dmin, 12 scale bytes) | q6_K: 16 int8 scales
-    u32x4 q[NQ];   // q4_K: 32 nibble bytes | q6_K raw: ql 32 B, qh 32 B | W_exp: unused
+    static constexpr int NQ = QT == 4 ? 2 : (ARM != ARM_RAW ? 1 : 4);
+    u32x4 h;       // q4_K header (d, dmin, 12 scale bytes) | q6_K: 16 int8 scales |
+                   // PREP: 16 bytes of the row's scale block
+    u32x4 q[NQ];   // q4_K: 32 nibble bytes | q6_K raw: ql 32 B, qh 32 B | q6_K dense arms: unused
     uint32_t d;    // q6_K fp16 d (low half)
     uint32_t ad[2];   // two activation block dwords (fp16 d in the low half)
     uint32_t as[2];   // q4_K: ssum of the same two blocks
@@ -174,11 +184,12 @@ struct Src {
     uint32_t aq[2];      // this lane's quant-half sources, token halves 0/1 of the tile
     uint32_t ad[2];      // blocks of this lane's two activation d (and ssum) loads
     uint32_t wo;         // this lane's weight row
+    uint32_t qo;         // q4_K PREP: this lane's row of the nibble plane
     uint32_t xq[2];      // this lane's W_exp copy sources, row halves 0/1 of the tile
     int64_t wstep;       // bytes per super-block along w
 };
 
-template <int QT, bool WEXP>
+template <int QT, int ARM>
 __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t jw0)
 {
     Src s;
@@ -212,12 +223,15 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
     // Weight staging: lanes l and l+16k of a wave take rows 16w + l%16, so a
     // load covers 16 rows (not 64) and the LDS writes stay conflict free.
     const uint32_t jl = (uint32_t)(min(jw0 + 16 * (tid >> 6) + (tid & 15), g.od - 1) - jw0);
-    s.wstep = QT == 4 ? 144 : g.bstride;
+    // PREP: W is the scale plane, 64 bytes per (row, super-block)
+    s.wstep = ARM == ARM_PREP ? 64 : (QT == 4 ? 144 : g.bstride);
     s.w = g.W + jw0 * nsb * s.wstep;
     s.wo = jl * (uint32_t)(nsb * s.wstep);
     // W_exp copies: the same mapping as the activation quant copies, with
     // weight rows in place of tokens (a row's chunk is 32 plain bytes).
-    s.x = WEXP ? g.Wexp + jw0 * g.id : nullptr;
+    // q4_K PREP: nibble plane, id/2 bytes per row, 128 per super-block
+    s.x = ARM == ARM_RAW ? nullptr : g.Wexp + jw0 * (QT == 4 ? g.id / 2 : g.id);
+    s.qo = jl * (uint32_t)(g.id / 2);
     {
         const int l = tid & 63;
 #pragma unroll
@@ -249,9 +263,10 @@ __device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb
     }
 }
 
-// q6_K dense arm: direct global->LDS copies of super-block sb's quants from
-// W_exp into stage b (same completion rule as load_act).
-__device__ __forceinline__ void load_wexp(Stage<6> &st, const Src &s, int64_t sb)
+// Dense arms: direct global->LDS copies of super-block sb's quants from the
+// quant plane into stage b (same completion rule as load_act).
+template <int QT>
+__device__ __forceinline__ void load_wexp(Stage<QT> &st, const Src &s, int64_t sb)
 {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const uint8_t *x = s.x + sb * 256;
@@ -263,8 +278,8 @@ __device__ __forceinline__ void load_wexp(Stage<6> &st, const Src &s, int64_t sb
     }
 }
 
-template <int QT, bool WEXP>
-__device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t sb)
+template <int QT, int ARM>
+__device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t sb)
 {
     const int part = (threadIdx.x >> 4) & 3;
     const uint8_t *q8 = s.q8 + sb * 320;
@@ -275,13 +290,20 @@ __device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t
         r.as[1] = *reinterpret_cast<const uint32_t *>(q8 + 36 + s.ad[1]);
     }
     const uint8_t *blk = s.w + sb * s.wstep + s.wo;
-    if constexpr (QT == 4) {
+    if constexpr (ARM == ARM_PREP) {
+        r.h = ld16(blk + 16 * part);
+        if constexpr (QT == 4) {
+            const uint8_t *q = s.x + sb * 128 + s.qo + 32 * part;   // nibble group `part`
+            r.q[0] = ld16(q);
+            r.q[1] = ld16(q + 16);
+        }
+    } else if constexpr (QT == 4) {
         r.h = ld16(blk);
         r.q[0] = ld16(blk + 16 + 32 * part);
         r.q[1] = ld16(blk + 32 + 32 * part);
     } else {
         const int h = part >> 1, pp = part & 1;
-        if constexpr (!WEXP) {
+        if constexpr (ARM == ARM_RAW) {
             r.q[0] = ld16(blk + 64 * h + 32 * pp);        // ql bytes of quarters pp, pp+2
             r.q[1] = ld16(blk + 64 * h + 32 * pp + 16);
             r.q[2] = ld16(blk + 128 + 32 * h);            // qh bytes of this half
@@ -292,8 +314,8 @@ __device__ __forceinline__ void load_raw(Raw<QT, WEXP> &r, const Src &s, int64_t
     }
 }
 
-template <int QT, bool WEXP>
-__device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
+template <int QT, int ARM>
+__device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r)
 {
     const int tid = threadIdx.x;
     const int row = 16 * (tid >> 6) + (tid & 15), part = (tid >> 4) & 3;
@@ -318,6 +340,26 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
         st16(&s.b[2 * part][row][16 * (1 ^ sw)], w1 & 0x0F0F0F0Fu);
         st16(&s.b[2 * part + 1][row][16 * (0 ^ sw)], (w0 >> 4) & 0x0F0F0F0Fu);
         st16(&s.b[2 * part + 1][row][16 * (1 ^ sw)], (w1 >> 4) & 0x0F0F0F0Fu);
+    }
+    if constexpr (ARM == ARM_PREP) {
+        // this lane's 16 bytes of the row's scale block
+        if constexpr (QT == 4) {
+            // part p: (d*sc, dmin*m) of sub-blocks 2p and 2p+1; the min-term
+            // pair lands in K half p/2, elements 2(p%2), 2(p%2)+1
+            uint16_t hi0, lo0, hi1, lo1;
+            s.bs[2 * part][row] = as_float((int)r.h[0]);
+            s.bs[2 * part + 1][row] = as_float((int)r.h[2]);
+            bf16_split(as_float((int)r.h[1]), hi0, lo0);
+            bf16_split(as_float((int)r.h[3]), hi1, lo1);
+            uint32_t *mm = s.mb[row][part >> 1].w;
+            mm[part & 1] = hi0 | (uint32_t)hi1 << 16;
+            mm[2 + (part & 1)] = lo0 | (uint32_t)lo1 << 16;
+        } else {
+            // part p: d*sc of sub-blocks 4p .. 4p+3 = chunks 2p, 2p+1
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s.bs[2 * part + (k >> 1)][row][k & 1] = as_float((int)r.h[k]);
+        }
+    } else if constexpr (QT == 4) {
         // scale/min of sub-blocks part (< 4) and part + 4 from the twelve
         // packed bytes S[0..11] = header bytes 4..15: byte `part` of each of
         // the three scale dwords.
@@ -344,7 +386,7 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, WEXP> &r)
         for (int z = 0; z < 2; ++z) {
             const int qq = pp + 2 * z;          // quarter of the half
             const int c = 4 * h + qq;
-            if constexpr (!WEXP) {
+            if constexpr (ARM == ARM_RAW) {
                 u32x4 o[2];
                 // quarter qq: nibble z of ql, bits 2qq..2qq+1 of qh moved to 4..5
                 const int lsh = 4 - 2 * pp;    // z = 0: qh << (4 - 2pp); z = 1: qh >> 2pp
@@ -488,7 +530,7 @@ __device__ __forceinline__ void epilogue(const ChunkD<QT> &D, const Sc<QT> &o, c
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int QT, bool WEXP, int MODE>
+template <int QT, int ARM, int MODE>
 __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 {
     __shared__ Stage<QT> st[2];
@@ -529,7 +571,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
         accm[i] = 0.0f;
     }
 
-    const Src src = make_src<QT, WEXP>(g, tw0, jw0);
+    const Src src = make_src<QT, ARM>(g, tw0, jw0);
     if constexpr (QT == 6) {
         // the zero rows of both stages (2 x 8 x 32 bytes)
         if (threadIdx.x < 32) {
@@ -537,9 +579,9 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             *reinterpret_cast<u32x4 *>(&st[k >> 4].a[(k >> 1) & 7][TT][16 * (k & 1)]) = u32x4{0, 0, 0, 0};
         }
     }
-    Raw<QT, WEXP> rw;
+    Raw<QT, ARM> rw;
     load_act(st[0], src, 0);
-    if constexpr (WEXP) load_wexp(st[0], src, 0);
+    if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[0], src, 0);
     load_raw(rw, src, 0);
     store_raw(st[0], rw);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the activation copy has landed
@@ -550,7 +592,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
         const bool more = sb + 1 < nsb;
         if (more) {
             load_act(st[(sb + 1) & 1], src, sb + 1);
-            if constexpr (WEXP) load_wexp(st[(sb + 1) & 1], src, sb + 1);
+            if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[(sb + 1) & 1], src, sb + 1);
             load_raw(rw, src, sb + 1);
         }
 
@@ -613,7 +655,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 // ---------------------------------------------------------------------------
 // host-side launchers (argument checking is done by the C ABI layer)
 // ---------------------------------------------------------------------------
-template <int QT, bool WEXP, int MODE>
+template <int QT, int ARM, int MODE>
 static int launch(MmqArgs g, hipStream_t stream)
 {
     const int64_t nbt = (g.t1 - g.t0 + TT - 1) / TT;
@@ -621,7 +663,7 @@ static int launch(MmqArgs g, hipStream_t stream)
     if (nbt <= 0 || nbj <= 0) return 0;
     if (nbt * nbj > 0x7fffffff) return -1;
     g.nbt = (int)nbt;
-    hipLaunchKernelGGL((mmq_kernel<QT, WEXP, MODE>), dim3((unsigned)(nbt * nbj)), dim3(NTHR), 0,
+    hipLaunchKernelGGL((mmq_kernel<QT, ARM, MODE>), dim3((unsigned)(nbt * nbj)), dim3(NTHR), 0,
                        stream, g);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
@@ -645,11 +687,16 @@ int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
     g.j1 = Lc.j1;
     g.nbt = 0;
     const bool part = Lc.P != nullptr;
-    if (Lc.qtype == 4)
-        return part ? launch<4, false, 1>(g, stream) : launch<4, false, 0>(g, stream);
+    if (Lc.qtype == 4) {
+        if (Lc.prepared)
+            return part ? launch<4, ARM_PREP, 1>(g, stream) : launch<4, ARM_PREP, 0>(g, stream);
+        return part ? launch<4, ARM_RAW, 1>(g, stream) : launch<4, ARM_RAW, 0>(g, stream);
+    }
+    if (Lc.prepared)
+        return part ? launch<6, ARM_PREP, 1>(g, stream) : launch<6, ARM_PREP, 0>(g, stream);
     if (Lc.Wexp)
-        return part ? launch<6, true, 1>(g, stream) : launch<6, true, 0>(g, stream);
-    return part ? launch<6, false, 1>(g, stream) : launch<6, false, 0>(g, stream);
+        return part ? launch<6, ARM_WEXP, 1>(g, stream) : launch<6, ARM_WEXP, 0>(g, stream);
+    return part ? launch<6, ARM_RAW, 1>(g, stream) : launch<6, ARM_RAW, 0>(g, stream);
 }
 
 }  // namespace qig

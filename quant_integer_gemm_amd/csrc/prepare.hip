@@ -1,0 +1,102 @@
+// prepare.hip -- registration-time "prepared" weight buffers for the MMQ.
+//
+// A prepared buffer trades device memory for work in the GEMM: its scales
+// are already fp32 products and its quants need no bit-field recombination.
+// Layout:
+//   quant plane  q6_K: Q[j*id + 256*sb + e], one centred int8 per element
+//                (as expand_q6k_dense writes it), row stride id;
+//                q4_K: the 128 packed nibble bytes of each block, as in the
+//                raw block, at Q[j*id/2 + 128*sb + i] (row stride id/2) --
+//                a byte per element would double the bytes the GEMM loads
+//                and measured slower than splitting nibbles in registers
+//   scale plane  S[(j*nsb + sb)*16 + k]          fp32, 64 bytes per block
+//     q4_K: k = 2b     -> d * sc_b     (b = 0..7, 32-element sub-blocks)
+//           k = 2b + 1 -> dmin * m_b   (so each 16-byte piece is complete
+//                                       for two sub-blocks)
+//     q6_K: k = s      -> d * sc_s     (s = 0..15, 16-element sub-blocks)
+// The products are formed exactly as the raw-block GEMM forms them (fp16 d
+// widened to fp32, times the integer scale, one fp32 rounding), so a GEMM on
+// a prepared buffer gives bit-identical output to one on the raw blocks.
+#include "qig_device.h"
+#include "qig_launch.h"
+
+namespace qig {
+
+// q4_K: one thread per (row, super-block, 64-element group g): the group's 32
+// nibble bytes copied, plus the scales of sub-blocks 2g and 2g+1.
+__global__ __launch_bounds__(256) void prepare_q4k_kernel(const uint8_t *__restrict__ W, int64_t od,
+                                                           int64_t id, uint8_t *__restrict__ Q,
+                                                           float *__restrict__ S)
+{
+    const int64_t nsb = id / 256;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= od * nsb * 4) return;
+    const int grp = (int)(gid & 3);
+    const int64_t blkno = gid >> 2;                 // j * nsb + sb
+    const int64_t j = blkno / nsb, sb = blkno % nsb;
+    const uint8_t *blk = W + blkno * 144;
+    const u32x4 hdr = *reinterpret_cast<const u32x4 *>(blk);
+    const u32x4 q0 = *reinterpret_cast<const u32x4 *>(blk + 16 + 32 * grp);
+    const u32x4 q1 = *reinterpret_cast<const u32x4 *>(blk + 32 + 32 * grp);
+    uint8_t *dst = Q + j * (id / 2) + 128 * sb + 32 * grp;
+    *reinterpret_cast<u32x4 *>(dst) = q0;
+    *reinterpret_cast<u32x4 *>(dst + 16) = q1;
+    uint8_t sbytes[12];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) sbytes[k] = (uint8_t)(hdr[1 + (k >> 2)] >> (8 * (k & 3)));
+    const float d = h2f(hdr[0]), dmin = h2f(hdr[0] >> 16);
+    float *s = S + blkno * 16;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int b = 2 * grp + k;
+        int sc, m;
+        q4_scale_min(sbytes, b, sc, m);
+        s[2 * b] = d * (float)sc;
+        s[2 * b + 1] = dmin * (float)m;
+    }
+}
+
+// q6_K scale plane: one thread per (row, super-block).
+__global__ __launch_bounds__(256) void prepare_q6k_scales_kernel(const uint8_t *__restrict__ W, int64_t bstride,
+                                                                  int64_t od, int64_t id, float *__restrict__ S)
+{
+    const int64_t nsb = id / 256;
+    const int64_t blkno = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // j * nsb + sb
+    if (blkno >= od * nsb) return;
+    const uint8_t *blk = W + blkno * bstride;
+    const u32x4 sc = *reinterpret_cast<const u32x4 *>(blk + 192);
+    const float d = h2f(*reinterpret_cast<const uint32_t *>(blk + 208));
+    float *s = S + blkno * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = d * (float)(int8_t)((sc[q] >> (8 * e)) & 0xff);
+        *reinterpret_cast<f32x4 *>(s + 4 * q) = v;
+    }
+}
+
+int launch_prepare_q4k(const void *W, int64_t od, int64_t id, int8_t *Q, float *S, hipStream_t stream)
+{
+    const int64_t n = od * (id / 256) * 4;
+    if (n == 0) return 0;
+    const int64_t grid = (n + 255) / 256;
+    if (grid > 0x7fffffff) return -1;
+    hipLaunchKernelGGL(prepare_q4k_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint8_t *>(W), od, id, reinterpret_cast<uint8_t *>(Q), S);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_prepare_q6k_scales(const void *W, int64_t bstride, int64_t od, int64_t id, float *S,
+                              hipStream_t stream)
+{
+    const int64_t n = od * (id / 256);
+    if (n == 0) return 0;
+    const int64_t grid = (n + 255) / 256;
+    if (grid > 0x7fffffff) return -1;
+    hipLaunchKernelGGL(prepare_q6k_scales_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint8_t *>(W), bstride, od, id, S);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace qig

@@ -8,13 +8,14 @@ namespace qig {
 
 struct MmqLaunch {
     int qtype;               // 4 (q4_K) or 6 (q6_K)
-    const void *W;           // raw blocks
-    const int8_t *Wexp;      // q6_K dense plane or nullptr
+    const void *W;           // raw blocks; prepared: the scale plane
+    const int8_t *Wexp;      // q6_K dense plane or nullptr; prepared: the quant plane
     const void *q8;          // pad40 activations
     float *y;                // output (GEMM mode) or nullptr
     int32_t *P;              // partials (test mode) or nullptr
     int64_t bstride, od, id, nt, ldy;
     int64_t t0, t1, j0, j1;  // output window
+    bool prepared = false;   // W / Wexp point into a prepared buffer
 };
 
 // All return 0, -1 (grid too large) or -3 (launch error).
@@ -23,5 +24,12 @@ int launch_quantize(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q
                     hipStream_t stream);
 int launch_expand_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, int8_t *Wexp,
                       hipStream_t stream);
+// Prepared buffers: quant plane (q6_K: [od][id] centred int8; q4_K:
+// [od][id/2] packed nibble bytes), then scale plane [od][id/256][16] fp32
+// (q4_K: d*sc and dmin*m of each of the 8 sub-blocks, in pairs; q6_K: d*sc
+// of the 16).
+int launch_prepare_q4k(const void *W, int64_t od, int64_t id, int8_t *Q, float *S, hipStream_t stream);
+int launch_prepare_q6k_scales(const void *W, int64_t bstride, int64_t od, int64_t id, float *S,
+                              hipStream_t stream);
 
 }  // namespace qig

@@ -22,7 +22,8 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ["quantize_q8_pad40", "mmq_q4k", "mmq_q6k", "expand_q6k_dense", "q8_pad40_bytes",
-              "qig_strerror", "mmq_q4k_partials", "mmq_q6k_partials"]:
+              "qig_strerror", "mmq_q4k_partials", "mmq_q6k_partials", "q4k_prepared_bytes",
+              "q6k_prepared_bytes", "prepare_q4k", "prepare_q6k", "mmq_q4k_prepared", "mmq_q6k_prepared"]:
         assert n in names
 
 
@@ -121,3 +122,21 @@ def test_oracle_not_imported_by_product():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "qig_oracle" not in text, f
+
+
+def test_prepared_sizes_and_argument_checks():
+    lib = qig.load()
+    assert qig.prepared_bytes("q4_K", 3584, 3584) == 3584 * 1792 + 3584 * 14 * 64
+    assert qig.prepared_bytes("q6_K", 256, 512) == 256 * 512 + 256 * 2 * 64
+    assert lib.q4k_prepared_bytes(4, 100) == 0
+    assert lib.q6k_prepared_bytes(-1, 256) == 0
+    assert lib.prepare_q4k(A16, 4, 100, B16, None) == -1          # id % 256
+    assert lib.prepare_q4k(MIS, 4, 256, B16, None) == -2
+    assert lib.prepare_q4k(A16, 4, 256, MIS, None) == -2
+    assert lib.prepare_q4k(A16, 0, 256, B16, None) == 0
+    assert lib.prepare_q6k(A16, 200, 4, 256, B16, None) == -1     # bstride
+    assert lib.prepare_q6k(A16, 224, 4, 256, MIS, None) == -2
+    assert lib.mmq_q4k_prepared(A16, 8, 100, B16, 4, A16, 8, None) == -1   # id % 256
+    assert lib.mmq_q4k_prepared(MIS, 8, 256, B16, 4, A16, 8, None) == -2
+    assert lib.mmq_q6k_prepared(A16, 8, 256, B16, 4, A16, 4, None) == -1   # ldy < od
+    assert lib.mmq_q6k_prepared(A16, 8, 256, B16, 0, A16, 8, None) == 0    # nt == 0

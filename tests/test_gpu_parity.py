@@ -2,7 +2,7 @@
 
 Bars: pad40 bytes, W_exp bytes and int32 sub-block partials bit-exact; fp32 y
 within |y - y_ref| <= max(1e-4 |y_ref|, 1e-3 rms(y_ref)) per element, y_ref
-being the oracle's fp64 result.  Shapes span several tiles (64 tokens x 128
+being the oracle's fp64 result.  Shapes span several tiles (64 tokens x 64
 rows per workgroup) with ragged tails, the five workloads at full size (all
 outputs for the nt=512 GEMMs, sampled outputs for the nt=2630 layer), and the
 degenerate cases (empty inputs, one token, one row).
@@ -236,6 +236,75 @@ def _run_workload_gemm(qig, gm, seed, sample=None):
     rms = float(np.sqrt(np.mean(y.astype(np.float64) ** 2)))
     ok, worst = oracle.within_tolerance(y[tt, jj], ref, rms=rms)
     assert ok, f"{gm.name}: worst error/allowance = {worst:.3g}"
+
+
+# ---------------------------------------------------------------------------
+# prepared weights (registration-time quant + scale planes)
+# ---------------------------------------------------------------------------
+def _prepared_expected(qtype, W, od, id_):
+    """Quant plane and fp32 scale plane from the oracle's block decoders
+    (q4_K quant plane: the raw blocks' packed quant bytes, 128 per block)."""
+    nsb = id_ // 256
+    Q = np.zeros((od, id_ // 2 if qtype == "q4_K" else id_), dtype=np.int8)
+    S = np.zeros((od, nsb, 16), dtype=np.float32)
+    if qtype == "q6_K":
+        Q[:] = oracle.expand_q6k_dense(W, 224, od, id_)
+        Wb = W.reshape(od, nsb, 224)
+        for j in range(od):
+            for sb in range(nsb):
+                _, sc, d = oracle.q6k_decode_block(Wb[j, sb])
+                S[j, sb] = (d * sc.astype(np.float64)).astype(np.float32)   # exact products
+    else:
+        Wb = W.reshape(od, nsb, 144)
+        for j in range(od):
+            for sb in range(nsb):
+                q, sc, m, d, dmin = oracle.q4k_decode_block(Wb[j, sb])
+                qs = Wb[j, sb, 16:144]
+                # the packed bytes decode to the oracle's elements (low nibble
+                # of byte 32g+i = element 64g+i, high nibble = 64g+32+i)
+                g_, i_ = np.divmod(np.arange(128), 32)
+                assert np.array_equal(qs & 15, q[64 * g_ + i_]) and np.array_equal(qs >> 4, q[64 * g_ + 32 + i_])
+                Q[j, 128 * sb:128 * sb + 128] = qs.view(np.int8)
+                S[j, sb, 0::2] = (d * sc.astype(np.float64)).astype(np.float32)
+                S[j, sb, 1::2] = (dmin * m.astype(np.float64)).astype(np.float32)
+    return Q, S
+
+
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("od,id_", [(130, 768), (64, 256)])
+def test_prepared_planes_content(qig, qtype, od, id_):
+    gm = inputs.Gemm("prep", qtype, od, id_, 1)
+    W, _ = inputs.make_gemm_inputs(gm, inputs.SEED_BASE + 300 + od)
+    if qtype == "q6_K":
+        Wp = host(qig.prepare_q6k(dev(W), 224, od, id_))
+    else:
+        Wp = host(qig.prepare_q4k(dev(W), od, id_))
+    assert Wp.size == qig.prepared_bytes(qtype, od, id_)
+    Q, S = _prepared_expected(qtype, W, od, id_)
+    assert np.array_equal(Wp[:Q.size].view(np.int8).reshape(Q.shape), Q)
+    got = Wp[Q.size:].view(np.float32).reshape(S.shape)
+    assert np.array_equal(got.view(np.uint32), S.view(np.uint32))
+
+
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("nt,od,id_", [(16, 256, 512), (70, 130, 768), (129, 257, 512), (1, 1, 256),
+                                       (512, 3584, 3584)])
+def test_prepared_gemm_matches_raw_bitwise(qig, qtype, nt, od, id_):
+    gm = inputs.Gemm("prep", qtype, od, id_, nt)
+    W, x = inputs.make_gemm_inputs(gm, inputs.SEED_BASE + 400 + nt)
+    q8d = qig.quantize_q8_pad40(dev(x))
+    Wd = dev(W)
+    if qtype == "q6_K":
+        y_raw = qig.mmq_q6k(Wd, 224, od, id_, q8d, nt)
+        y_prep = qig.mmq_q6k_prepared(qig.prepare_q6k(Wd, 224, od, id_), od, id_, q8d, nt)
+    else:
+        y_raw = qig.mmq_q4k(Wd, od, id_, q8d, nt)
+        y_prep = qig.mmq_q4k_prepared(qig.prepare_q4k(Wd, od, id_), od, id_, q8d, nt)
+    y_raw, y_prep = host(y_raw), host(y_prep)
+    assert np.array_equal(y_prep.view(np.uint32), y_raw.view(np.uint32))
+    if nt * od <= 70 * 130:
+        q8 = oracle.quantize_q8_pad40(x)
+        _assert_close(y_prep, _oracle_gemm(qtype, W, od, id_, q8, nt), f"prepared {qtype} {nt}x{od}x{id_}")
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3])
