@@ -7,7 +7,9 @@ the q-projection shape (od = id = 3584, nt = 512):
     quantize_q8_pad40(x6) -> mmq_q6k(W6)            (q6_K GEMM, raw blocks)
                           -> mmq_q6k(W6, W_exp)     (q6_K GEMM, dense-plane arm)
 Inputs are resident in HBM before timing; the dense plane is built once
-beforehand (it is registration-time work) and timed separately.
+beforehand (it is registration-time work) and timed separately, as are the
+prepared-buffer GEMMs (registration-time quant + fp32 scale planes), which are
+reported per kernel but are not part of the step.
 
 Prints one JSON line: value = int8 TOPS of the whole step (3 GEMMs x
 2*nt*od*id ops / step time), the per-kernel average durations from HIP
@@ -125,17 +127,28 @@ def main():
     y6 = torch.empty((NT, OD), dtype=torch.float32, device=dev)
     y6e = torch.empty((NT, OD), dtype=torch.float32, device=dev)
     wexp = torch.empty((OD, ID), dtype=torch.int8, device=dev)
+    W4p = torch.empty(qig.prepared_bytes("q4_K", OD, ID), dtype=torch.uint8, device=dev)
+    W6p = torch.empty(qig.prepared_bytes("q6_K", OD, ID), dtype=torch.uint8, device=dev)
 
-    # registration-time expansion, timed on its own
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for _ in range(3):
-        qig.expand_q6k_dense(W6d, 224, OD, ID, out=wexp)
-    ev[0].record()
-    for _ in range(10):
-        qig.expand_q6k_dense(W6d, 224, OD, ID, out=wexp)
-    ev[1].record()
-    torch.cuda.synchronize()
-    expand_us = ev[0].elapsed_time(ev[1]) * 1e3 / 10
+    # registration-time work, each timed on its own
+    def time_us(fn, reps=10):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    registration_us = {
+        "expand_q6k_dense": time_us(lambda: qig.expand_q6k_dense(W6d, 224, OD, ID, out=wexp)),
+        "prepare_q4k": time_us(lambda: qig.prepare_q4k(W4d, OD, ID, out=W4p)),
+        "prepare_q6k": time_us(lambda: qig.prepare_q6k(W6d, 224, OD, ID, out=W6p)),
+    }
+    y4p = torch.empty((NT, OD), dtype=torch.float32, device=dev)
+    y6p = torch.empty((NT, OD), dtype=torch.float32, device=dev)
 
     names = ["quantize_x4", "mmq_q4k", "quantize_x6", "mmq_q6k_raw", "mmq_q6k_wexp"]
     calls = [
@@ -182,6 +195,11 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         per[n] = e0.elapsed_time(e1) * 1e3 / args.steps
+    # the prepared-buffer arms (not part of the step), timed the same way
+    extra = {"mmq_q4k_prepared": lambda: qig.mmq_q4k_prepared(W4p, OD, ID, q84, NT, y=y4p, ldy=OD),
+             "mmq_q6k_prepared": lambda: qig.mmq_q6k_prepared(W6p, OD, ID, q86, NT, y=y6p, ldy=OD)}
+    for n, fn in extra.items():
+        per[n] = time_us(fn, reps=args.steps)
 
     gemm_ops = 2.0 * NT * OD * ID
     value = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
@@ -212,11 +230,11 @@ def main():
             "nt": NT, "od": OD, "id": ID, "seeds": [SEED4, SEED6],
         },
         "per_kernel_us": {k: round(v, 3) for k, v in per.items()},
-        "per_gemm_tops": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12, 1) for n in gemms},
+        "per_gemm_tops": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12, 1) for n in gemms + list(extra)},
         "per_gemm_pct_int8_peak": {n: round(100 * gemm_ops / (per[n] * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2)
                                    for n in gemms},
         "per_gemm_hbm_gbs": {n: round((wbytes[n] + abytes) / (per[n] * 1e-6) / 1e9, 1) for n in gemms},
-        "expand_q6k_dense_us": round(expand_us, 3),
+        "registration_us": {k: round(v, 3) for k, v in registration_us.items()},
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
