@@ -161,6 +161,44 @@ int mmq_q6k_prepared(const void *Wp, int64_t od, int64_t id, const void *q8,
                      int64_t nt, float *y, int64_t ldy, hipStream_t stream);
 
 /*
+ * Stream-K variants -- the same GEMMs, with the work split by super-block
+ * when the 64 x 64 output tiles leave much of the GPU idle (the pages'
+ * reference launches a stream-k grid plus a fix-up kernel for the q-proj
+ * shape: r20 page "Split-phase A staging", s1 and s2.2).  When the tiles
+ * form a single round that fills at most three quarters of the workgroup
+ * slots (two per CU), the (tile, super-block) iterations are shared evenly
+ * by all slots, and a tile split between workgroups is summed from their
+ * partial sums in a fixed order, so y is the same on every call (it may
+ * differ from the plain call's y by fp32 rounding order, within the output
+ * tolerance).  Other shapes, and id < 512, run exactly as the plain calls:
+ * on them whole tiles measured faster.
+ *
+ *   ws     mmq_workspace_bytes() bytes of device memory, 16-byte aligned,
+ *          owned by the caller and ZERO-FILLED ONCE before its first use.
+ *          It holds partial sums (written before they are read) and, in
+ *          its last 16384 bytes, arrival counters that every call returns to
+ *          zero; do not write to it between calls.  Calls that may run at
+ *          the same time (different streams) need different workspaces;
+ *          calls in order on one stream may share one.
+ *   other arguments as the plain call of the same name.
+ * Errors: as the plain call, plus QIG_EINVAL for ws == NULL and QIG_EALIGN
+ *         for a misaligned ws.
+ */
+size_t mmq_workspace_bytes(void);
+int mmq_q4k_streamk(const void *W, int64_t od, int64_t id, const void *q8,
+                    int64_t nt, float *y, int64_t ldy, void *ws,
+                    hipStream_t stream);
+int mmq_q6k_streamk(const void *W, int64_t bstride, const int8_t *W_exp,
+                    int64_t od, int64_t id, const void *q8, int64_t nt,
+                    float *y, int64_t ldy, void *ws, hipStream_t stream);
+int mmq_q4k_prepared_streamk(const void *Wp, int64_t od, int64_t id,
+                             const void *q8, int64_t nt, float *y, int64_t ldy,
+                             void *ws, hipStream_t stream);
+int mmq_q6k_prepared_streamk(const void *Wp, int64_t od, int64_t id,
+                             const void *q8, int64_t nt, float *y, int64_t ldy,
+                             void *ws, hipStream_t stream);
+
+/*
  * Test exports: the int32 sub-block partials of the same kernels, for the
  * window of tokens [t0, t1) and rows [j0, j1), written to
  * P[(t - t0)][(j - j0)][sub] (int32, 4-byte aligned), where sub runs over all

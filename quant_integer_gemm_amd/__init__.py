@@ -12,13 +12,19 @@ from ._lib import (  # noqa: F401
     load,
     mmq_q4k,
     mmq_q4k_partials,
-    mmq_q6k,
     mmq_q4k_prepared,
+    mmq_q4k_prepared_streamk,
+    mmq_q4k_streamk,
+    mmq_q6k,
     mmq_q6k_partials,
     mmq_q6k_prepared,
+    mmq_q6k_prepared_streamk,
+    mmq_q6k_streamk,
+    new_workspace,
     prepare_q4k,
     prepare_q6k,
     prepared_bytes,
     q8_pad40_bytes,
     quantize_q8_pad40,
+    workspace,
 )

@@ -35,6 +35,11 @@ SIGNATURES = {
     "prepare_q6k": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "mmq_q4k_prepared": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
     "mmq_q6k_prepared": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "mmq_workspace_bytes": (ctypes.c_size_t, []),
+    "mmq_q4k_streamk": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "mmq_q6k_streamk": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "mmq_q4k_prepared_streamk": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "mmq_q6k_prepared_streamk": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
 }
 
 
@@ -195,4 +200,70 @@ def mmq_q6k_prepared(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
     _check(load().mmq_q6k_prepared(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
                                    _stream(stream)), "mmq_q6k_prepared")
+    return y
+
+
+# --- stream-K variants -------------------------------------------------------
+
+_workspaces = {}
+
+
+def workspace(device=None):
+    """The default stream-K workspace of a device: mmq_workspace_bytes() zero bytes,
+    allocated on first use and kept.  It serves calls issued in order on one stream;
+    calls that may overlap on different streams each need a workspace of their own
+    (``new_workspace``)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = new_workspace(dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def new_workspace(device):
+    """A fresh zero-filled stream-K workspace (uint8, mmq_workspace_bytes() bytes)."""
+    import torch
+    return torch.zeros(int(load().mmq_workspace_bytes()), dtype=torch.uint8, device=device)
+
+
+def mmq_q4k_streamk(W, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, ws=None, stream=None):
+    """mmq_q4k with the work split by super-block over all CUs (stream-K)."""
+    y, ldy = _out_y(y, nt, od, ldy, W.device)
+    ws = workspace(W.device) if ws is None else ws
+    _check(load().mmq_q4k_streamk(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
+                                  _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_streamk")
+    return y
+
+
+def mmq_q6k_streamk(W, bstride: int, od: int, id_: int, q8, nt: int, W_exp=None, y=None, ldy: int | None = None,
+                    ws=None, stream=None):
+    """mmq_q6k with the work split by super-block over all CUs (stream-K)."""
+    y, ldy = _out_y(y, nt, od, ldy, W.device)
+    ws = workspace(W.device) if ws is None else ws
+    _check(load().mmq_q6k_streamk(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_,
+                                  _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy, _dev_ptr(ws, "ws"),
+                                  _stream(stream)), "mmq_q6k_streamk")
+    return y
+
+
+def mmq_q4k_prepared_streamk(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, ws=None,
+                             stream=None):
+    """mmq_q4k_prepared, stream-K."""
+    y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    ws = workspace(Wp.device) if ws is None else ws
+    _check(load().mmq_q4k_prepared_streamk(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"),
+                                           ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_prepared_streamk")
+    return y
+
+
+def mmq_q6k_prepared_streamk(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, ws=None,
+                             stream=None):
+    """mmq_q6k_prepared, stream-K."""
+    y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    ws = workspace(Wp.device) if ws is None else ws
+    _check(load().mmq_q6k_prepared_streamk(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"),
+                                           ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_prepared_streamk")
     return y

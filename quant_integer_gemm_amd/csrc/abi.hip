@@ -68,24 +68,57 @@ int quantize_q8_pad40(const float *x, int64_t nt, int64_t id, int64_t ldx, void 
     return rc_from_launch(qig::launch_quantize(x, nt, id, ldx, q8, stream));
 }
 
-int mmq_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
-            hipStream_t stream)
+// ws: the stream-K workspace, or nullptr for whole tiles only.
+static int gemm_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
+                    void *ws, hipStream_t stream)
 {
     int rc = check_gemm(W, od, id, q8, nt, y, ldy, 144);
     if (rc != QIG_OK || nt == 0 || od == 0) return rc;
     qig::MmqLaunch L = {4, W, nullptr, q8, y, nullptr, 144, od, id, nt, ldy, 0, nt, 0, od};
+    L.ws = ws;
     return rc_from_launch(qig::launch_mmq(L, stream));
 }
 
-int mmq_q6k(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id, const void *q8,
-            int64_t nt, float *y, int64_t ldy, hipStream_t stream)
+static int gemm_q6k(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id,
+                    const void *q8, int64_t nt, float *y, int64_t ldy, void *ws, hipStream_t stream)
 {
     if (bad_bstride(bstride)) return QIG_EINVAL;
     int rc = check_gemm(W, od, id, q8, nt, y, ldy, bstride);
     if (rc != QIG_OK || nt == 0 || od == 0) return rc;
     if (W_exp && !aligned(W_exp, 16)) return QIG_EALIGN;
     qig::MmqLaunch L = {6, W, W_exp, q8, y, nullptr, bstride, od, id, nt, ldy, 0, nt, 0, od};
+    L.ws = ws;
     return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
+int mmq_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
+            hipStream_t stream)
+{
+    return gemm_q4k(W, od, id, q8, nt, y, ldy, nullptr, stream);
+}
+
+int mmq_q6k(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id, const void *q8,
+            int64_t nt, float *y, int64_t ldy, hipStream_t stream)
+{
+    return gemm_q6k(W, bstride, W_exp, od, id, q8, nt, y, ldy, nullptr, stream);
+}
+
+size_t mmq_workspace_bytes(void) { return (size_t)qig::MMQ_WS_BYTES; }
+
+int mmq_q4k_streamk(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
+                    void *ws, hipStream_t stream)
+{
+    if (!ws) return QIG_EINVAL;
+    if (!aligned(ws, 16)) return QIG_EALIGN;
+    return gemm_q4k(W, od, id, q8, nt, y, ldy, ws, stream);
+}
+
+int mmq_q6k_streamk(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id,
+                    const void *q8, int64_t nt, float *y, int64_t ldy, void *ws, hipStream_t stream)
+{
+    if (!ws) return QIG_EINVAL;
+    if (!aligned(ws, 16)) return QIG_EALIGN;
+    return gemm_q6k(W, bstride, W_exp, od, id, q8, nt, y, ldy, ws, stream);
 }
 
 int expand_q6k_dense(const void *W, int64_t bstride, int64_t od, int64_t id, int8_t *W_exp,
@@ -136,26 +169,43 @@ int prepare_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, void *Wp
 }
 
 static int mmq_prepared(int qtype, const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y,
-                        int64_t ldy, hipStream_t stream)
+                        int64_t ldy, void *ws, hipStream_t stream)
 {
     int rc = check_gemm(Wp, od, id, q8, nt, y, ldy, 64);
     if (rc != QIG_OK || nt == 0 || od == 0) return rc;
     const int8_t *Q = static_cast<const int8_t *>(Wp);
     const void *S = static_cast<const uint8_t *>(Wp) + prepared_quant_bytes(qtype, od, id);
     qig::MmqLaunch L = {qtype, S, Q, q8, y, nullptr, 64, od, id, nt, ldy, 0, nt, 0, od, true};
+    L.ws = ws;
     return rc_from_launch(qig::launch_mmq(L, stream));
 }
 
 int mmq_q4k_prepared(const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
                      hipStream_t stream)
 {
-    return mmq_prepared(4, Wp, od, id, q8, nt, y, ldy, stream);
+    return mmq_prepared(4, Wp, od, id, q8, nt, y, ldy, nullptr, stream);
 }
 
 int mmq_q6k_prepared(const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
                      hipStream_t stream)
 {
-    return mmq_prepared(6, Wp, od, id, q8, nt, y, ldy, stream);
+    return mmq_prepared(6, Wp, od, id, q8, nt, y, ldy, nullptr, stream);
+}
+
+int mmq_q4k_prepared_streamk(const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y,
+                             int64_t ldy, void *ws, hipStream_t stream)
+{
+    if (!ws) return QIG_EINVAL;
+    if (!aligned(ws, 16)) return QIG_EALIGN;
+    return mmq_prepared(4, Wp, od, id, q8, nt, y, ldy, ws, stream);
+}
+
+int mmq_q6k_prepared_streamk(const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y,
+                             int64_t ldy, void *ws, hipStream_t stream)
+{
+    if (!ws) return QIG_EINVAL;
+    if (!aligned(ws, 16)) return QIG_EALIGN;
+    return mmq_prepared(6, Wp, od, id, q8, nt, y, ldy, ws, stream);
 }
 
 int mmq_q4k_partials(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, int64_t t0,

@@ -11,14 +11,15 @@
 // Design (MI355X-first; the pages' IMMA kernels are prior art only):
 //  * A workgroup of 256 threads = 4 waves owns a 64-token x 64-row output
 //    tile, one 32x32 MFMA tile per wave.  Its double-buffered LDS stage is
-//    under 80 KB, so two workgroups share a CU and each SIMD runs two waves
+//    80 KB at most, so two workgroups share a CU and each SIMD runs two waves
 //    of different workgroups that do not move in lock-step.
 //  * MFMA rows are tokens and columns weight rows, so each lane owns one
 //    weight row: the per-(row, chunk) weight scale is a lane constant and the
-//    per-(token, chunk) fp16 activation scale a per-register value read from
-//    LDS as fp16 (v_fma_mix consumes it without conversion).
-//  * K advances one super-block (256) per step.  The raw blocks of step k+1
-//    are fetched with 16-byte loads while step k computes, then decoded
+//    per-(token, chunk) activation scale a per-register value, read from an
+//    fp32 table in LDS laid out in register order.
+//  * K advances one super-block (256) per step.  Step k+1's activation quants
+//    are copied global->LDS directly while step k computes; its weights (and
+//    the activation d / ssum values) are loaded to registers and decoded
 //    (nibbles / 6-bit recombination to int8, scales to fp32) into the other
 //    half of the LDS stage: one barrier per step.
 //  * Within a step a wave runs its 8 chunks as a software pipeline: the MFMA
@@ -26,14 +27,19 @@
 //    MFMA operands and chunk c+1's scales are fetched from LDS while it runs,
 //    and value pins keep the compiler from collapsing the pipeline.
 //  * Epilogue per 32-chunk: the int8 MFMA accumulates onto the 1.5*2^23 bias
-//    so one fma turns the int32 partial into P*w, rounded once; a v_fma_mix
-//    folds in the fp16 activation scale: 2 VALU ops per output and chunk for
-//    q4_K, 4 for q6_K (two 16-element sub-blocks, each its own MFMA with the
-//    other half of K zeroed).
-//  * q4_K min term: -dmin*m*ssum summed over chunks is a K = id/32 fp32 matrix
-//    product, done on the fp32 MFMA (32x32x2) into a second accumulator.
-//  * Workgroups are numbered so that each of the 8 XCDs (each with its own L2)
-//    gets a contiguous run of tiles: one slice of weight rows, all tokens.
+//    so one fma turns the int32 partial into P*w, rounded once; a second fma
+//    (three-operand form) folds in the activation scale: 2 VALU ops per
+//    output and chunk for q4_K, 4 for q6_K (two 16-element sub-blocks, each
+//    its own MFMA with the other half of K zeroed).
+//  * q4_K min term: -dmin*m*ssum summed over chunks is a K = id/32 matrix
+//    product, run per super-block on the bf16 MFMA with both factors split
+//    into bf16 hi/lo pairs, into a second accumulator.
+//  * Work: each workgroup (worker) runs a list of (tile, super-block range)
+//    items; whole tiles normally, or stream-K splits with a fixed-order
+//    fix-up when the tiles leave many workgroup slots empty.  Tiles are
+//    numbered in groups of 8 row tiles and workers XCD by XCD, so the tiles
+//    running on one XCD at a time share operands in its L2.
+#include <algorithm>
 #include <utility>
 
 #include "qig_device.h"
@@ -115,7 +121,13 @@ struct MmqArgs {
     int32_t *P;
     int64_t bstride, od, id, nt, ldy;
     int64_t t0, t1, j0, j1;   // output window (all of y for the GEMM)
-    int nbt;                  // token tiles in the window
+    int nbt, nbj;             // token and row tiles in the window
+    // Work decomposition (tiles numbered as tile_origin does): tiles below dp_tiles are
+    // whole-tile work items; the next sk_tiles are split into (tile,
+    // super-block) iterations shared evenly by the workers.
+    int dp_tiles, sk_tiles;   // both below 2^31, as is sk_tiles * (id / 256)
+    float *ws;                // split tiles: partial-sum slots, 2 per worker
+    uint32_t *cnt;            // split tiles: arrival counters, 1 per worker
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p)
@@ -190,10 +202,9 @@ struct Src {
 };
 
 template <int QT, int ARM>
-__device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t jw0)
+__device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t jw0, int tid)
 {
     Src s;
-    const int tid = threadIdx.x;
     const int64_t nb32 = g.id / 32, nsb = g.id / 256;
     // Activation copies (one super-block = 16 quant copies of 1 KB and 8 (q6_K)
     // or 16 (q4_K) dword copies of 256 bytes per workgroup).  Quant copy q of
@@ -245,43 +256,73 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// Direct global->LDS copy of 16 bytes per lane: lane l's bytes at
+// base + voff land at LDS byte address lds + 16 l (base and lds wave-
+// uniform).  It is issued from inline assembly because the compiler, unable
+// to tell the copy's LDS bytes from those the compute reads, otherwise waits
+// for every outstanding global load at the first such read, which kept each
+// step's loads from overlapping its compute.  The compiler therefore does
+// not know about these copies: their data is read only after an explicit
+// vmcnt(0) wait and a barrier, and since loads complete in order, extra
+// untracked loads only make the compiler's own counted waits stricter.  M0
+// (the LDS address register) is read when the copy issues and is restored
+// afterwards.
+__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, void *lds)
+{
+    // base and lds are wave-uniform; readfirstlane puts them in scalar
+    // registers, as the instruction requires, whatever the compiler infers.
+    // (readfirstlane returns a signed int: each half goes through uint32_t
+    // before it is widened, or an address with bit 31 set would sign-extend.)
+    const uint64_t b = reinterpret_cast<uintptr_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint64_t sbase = (uint64_t)lo | ((uint64_t)hi << 32);
+    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void_t *)lds);
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %3\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory");
+}
 
 // Direct global->LDS copies of super-block sb's activations into stage st.
 // The data lands asynchronously; a vmcnt(0) wait plus a barrier must come
 // before any wave reads it.
 template <int QT>
-__device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb)
+__device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb, int tid)
 {
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const uint8_t *q8 = s.q8 + sb * 320;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = 4 * w + i, c = q >> 1;
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(q8 + 40 * c + s.aq[i & 1]),
-                                         (lds_void_t *)(&st.a[c][32 * (q & 1)][0]), 16, 0, 0);
+        dma16(q8 + 40 * c, s.aq[i & 1], &st.a[c][32 * (q & 1)][0]);
     }
 }
 
 // Dense arms: direct global->LDS copies of super-block sb's quants from the
 // quant plane into stage b (same completion rule as load_act).
 template <int QT>
-__device__ __forceinline__ void load_wexp(Stage<QT> &st, const Src &s, int64_t sb)
+__device__ __forceinline__ void load_wexp(Stage<QT> &st, const Src &s, int64_t sb, int tid)
 {
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const uint8_t *x = s.x + sb * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = 4 * w + i, c = q >> 1;
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(x + 32 * c + s.xq[i & 1]),
-                                         (lds_void_t *)(&st.b[c][32 * (q & 1)][0]), 16, 0, 0);
+        dma16(x + 32 * c, s.xq[i & 1], &st.b[c][32 * (q & 1)][0]);
     }
 }
 
 template <int QT, int ARM>
-__device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t sb)
+__device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t sb, int tid)
 {
-    const int part = (threadIdx.x >> 4) & 3;
+    const int part = (tid >> 4) & 3;
     const uint8_t *q8 = s.q8 + sb * 320;
     r.ad[0] = *reinterpret_cast<const uint32_t *>(q8 + s.ad[0]);
     r.ad[1] = *reinterpret_cast<const uint32_t *>(q8 + s.ad[1]);
@@ -315,9 +356,8 @@ __device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t 
 }
 
 template <int QT, int ARM>
-__device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r)
+__device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r, int tid)
 {
-    const int tid = threadIdx.x;
     const int row = 16 * (tid >> 6) + (tid & 15), part = (tid >> 4) & 3;
     const int sw = swz(row);
 #pragma unroll
@@ -528,6 +568,148 @@ __device__ __forceinline__ void epilogue(const ChunkD<QT> &D, const Sc<QT> &o, c
 }
 
 // ---------------------------------------------------------------------------
+// Work items and the output of a tile.
+//
+// A worker (workgroup) runs a list of work items, each a tile and a run
+// [k0, k1) of its super-blocks: first whole tiles v, v + G, .. below
+// dp_tiles, then its share of the I = sk_tiles * nsb split-phase iterations
+// (stream-K), worker w taking iterations [floor(w I / G), floor((w+1) I / G))
+// in tile-major order.  A tile done by one item is stored straight to y.  A
+// split tile has contributors fw .. lw, consecutive workers.  Each wave owns
+// a 32 x 32 quarter of the tile and finishes it on its own: it writes its
+// partial sum to its worker's workspace slot and adds one to the quarter's
+// counter; the wave that brings the count to lw - fw + 1 adds the partials in
+// worker order fw, fw + 1, .., lw (its own from registers), stores y and puts
+// the counter back to zero.  The sum therefore does not depend on which
+// contributor finished last, and nothing waits on another workgroup.
+// ---------------------------------------------------------------------------
+struct Work {
+    int tile, k0, k1;   // k1 == 0: no more work
+};
+
+__device__ __forceinline__ Work next_work(const MmqArgs &g, int &dpt, int &it, int it_end, int G, int nsb)
+{
+    Work w;
+    if (dpt < g.dp_tiles) {
+        w.tile = dpt;
+        w.k0 = 0;
+        w.k1 = nsb;
+        dpt += G;
+    } else if (it < it_end) {
+        const int u = it / nsb;
+        w.tile = g.dp_tiles + u;
+        w.k0 = it - u * nsb;
+        w.k1 = min(nsb, w.k0 + (it_end - it));
+        it += w.k1 - w.k0;
+    } else {
+        w.tile = 0;
+        w.k0 = 0;
+        w.k1 = 0;
+    }
+    return w;
+}
+
+// Tile numbering: groups of TGROUP row tiles (the last group may be
+// narrower); within a group the row tile runs fastest.  Consecutive tile
+// numbers go to one XCD (see the worker numbering), so the 64 tiles an XCD
+// runs at once form an 8 x 8 block of token and row tiles that share their
+// activation and weight super-blocks in that XCD's L2, instead of one row
+// tile against every token tile (which made each XCD read the whole
+// activation plane).
+constexpr int TGROUP = 8;
+
+__device__ __forceinline__ void tile_origin(const MmqArgs &g, int tile, int64_t &tw0, int64_t &jw0)
+{
+    const int per = TGROUP * g.nbt;
+    const int grp = tile / per, r = tile - grp * per;
+    const int first = grp * TGROUP;
+    const int w = min(g.nbj - first, TGROUP);
+    tw0 = g.t0 + (int64_t)TT * (r / w);
+    jw0 = g.j0 + (int64_t)TJ * (first + r % w);
+}
+
+__device__ __forceinline__ void store_tile(const MmqArgs &g, const f32x16 &v, int64_t tw0, int64_t j,
+                                           const Lane &L)
+{
+    if (j < g.j1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t t = tw0 + 32 * L.wt + mfma_row(i, L.hh);
+            if (t < g.t1) g.y[t * g.ldy + j] = v[i];
+        }
+    }
+}
+
+// Worker owning split-phase iteration i.
+__device__ __forceinline__ int sk_worker(int i, int I, int G) { return (int)((((int64_t)i + 1) * G - 1) / I); }
+
+// Workspace slot of worker w's partial of split tile u (counted from the
+// first split tile): 2w for the tile holding w's first iteration, else 2w + 1
+// (a worker's iterations are contiguous, so only its first and last tiles can
+// be split).
+__device__ __forceinline__ int sk_slot(int u, int w, int I, int G, int nsb)
+{
+    return 2 * w + (u == (int)((int64_t)w * I / G) / nsb ? 0 : 1);
+}
+
+// The partial sums cross XCDs, whose L2 caches are not kept coherent with
+// each other.  Every access to them is an agent-scope atomic access, which
+// carries its own cache policy (stores write through to the device coherence
+// point, loads read from it), and a vmcnt(0) wait completes the stores before
+// the counter update.  A device-scope fence would do the same by writing back
+// and invalidating the whole L2 of the XCD, which measured several times the
+// cost of the GEMM itself when every split tile did it.
+__device__ __forceinline__ void st_agent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+__device__ __forceinline__ void finish_tile(const MmqArgs &g, const f32x16 &p, const Work &w, int v, int G,
+                                            int nsb, const Lane &L, int wave, int lane)
+{
+    int64_t tw0, jw0;
+    tile_origin(g, w.tile, tw0, jw0);
+    const int64_t j = jw0 + L.jb;
+    if (w.k0 == 0 && w.k1 == nsb) {
+        store_tile(g, p, tw0, j, L);
+        return;
+    }
+    const int u = w.tile - g.dp_tiles;
+    const int I = g.sk_tiles * nsb;
+    const int fw = sk_worker(u * nsb, I, G), lw = sk_worker((u + 1) * nsb - 1, I, G);
+    const int64_t quarter = 1024 * wave + lane;   // this lane's floats of the wave's quarter: + 64 i
+    float *mine = g.ws + (int64_t)sk_slot(u, v, I, G, nsb) * (TT * TJ) + quarter;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st_agent(mine + 64 * i, p[i]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the partial is at the coherence point
+    uint32_t *cnt = g.cnt + 4 * fw + wave;
+    uint32_t before = 0;
+    if (lane == 0) before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before != (uint32_t)(lw - fw)) return;   // another contributor finishes the quarter
+    f32x16 sum;
+    for (int c = fw; c <= lw; ++c) {
+        f32x16 q;
+        if (c == v) {
+            q = p;
+        } else {
+            float *src = g.ws + (int64_t)sk_slot(u, c, I, G, nsb) * (TT * TJ) + quarter;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) q[i] = ld_agent(src + 64 * i);
+        }
+        if (c == fw) {
+            sum = q;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum[i] += q[i];
+        }
+    }
+    store_tile(g, sum, tw0, j, L);
+    if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
 template <int QT, int ARM, int MODE>
@@ -535,136 +717,200 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 {
     __shared__ Stage<QT> st[2];
 
-    // XCD-aware numbering: consecutive blocks go round-robin to the 8 XCDs,
-    // so hand each XCD a contiguous run of tile indices.
+    // XCD-aware worker numbering: consecutive blocks go round-robin to the 8
+    // XCDs, so hand each XCD a contiguous run of worker numbers (and so of
+    // tiles).
     const int G = gridDim.x, b = blockIdx.x;
     const int q = G / 8, r = G % 8, x = b % 8;
-    const int tile = x * q + min(x, r) + b / 8;
-    const int bt = tile % g.nbt;
-    const int bj = tile / g.nbt;
-    const int64_t tw0 = g.t0 + (int64_t)TT * bt;   // workgroup tile origin
-    const int64_t jw0 = g.j0 + (int64_t)TJ * bj;
-    const int64_t nsb = g.id / 256;
+    const int v = x * q + min(x, r) + b / 8;
+    const int nsb = (int)(g.id / 256);
+    const int I = g.sk_tiles * nsb;   // the host keeps tile counts and I below 2^31
+    int it = (int)((int64_t)v * I / G);
+    const int it_end = (int)((int64_t)(v + 1) * I / G);
+    int dpt = v;
+    Work cur = next_work(g, dpt, it, it_end, G, nsb);
+    if (cur.k1 == 0) return;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    Lane L;
-    L.wt = wave & 1;                       // 32-token group of this wave
-    L.hh = lane >> 5;
-    L.ta = 32 * L.wt + (lane & 31);        // token (tile-local) this lane feeds to MFMA a
-    L.jb = 32 * (wave >> 1) + (lane & 31); // weight row (tile-local) of the lane
-    L.l16 = lane & 15;
-    {
-        const int own = 32 * L.ta + 16 * (L.hh ^ swz(L.ta)), zrow = 32 * TT;
-        L.pa0 = L.hh ? zrow : own;
-        L.pa1 = L.hh ? own : zrow;
-    }
-    const int64_t j = jw0 + L.jb;
-
-    i32x16 bias;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bias[i] = MAGIC_I;
-    f32x16 acc, accm;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        acc[i] = 0.0f;
-        accm[i] = 0.0f;
-    }
-
-    const Src src = make_src<QT, ARM>(g, tw0, jw0);
     if constexpr (QT == 6) {
-        // the zero rows of both stages (2 x 8 x 32 bytes)
+        // the zero rows of both stages (2 x 8 x 32 bytes); no copy writes them
         if (threadIdx.x < 32) {
             const int k = threadIdx.x;
             *reinterpret_cast<u32x4 *>(&st[k >> 4].a[(k >> 1) & 7][TT][16 * (k & 1)]) = u32x4{0, 0, 0, 0};
         }
     }
+
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    int64_t tw0, jw0;
+    tile_origin(g, cur.tile, tw0, jw0);
+    Src src = make_src<QT, ARM>(g, tw0, jw0, tid);
     Raw<QT, ARM> rw;
-    load_act(st[0], src, 0);
-    if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[0], src, 0);
-    load_raw(rw, src, 0);
-    store_raw(st[0], rw);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the activation copy has landed
-    __syncthreads();
-
-    for (int64_t sb = 0; sb < nsb; ++sb) {
-        const Stage<QT> &s = st[sb & 1];
-        const bool more = sb + 1 < nsb;
-        if (more) {
-            load_act(st[(sb + 1) & 1], src, sb + 1);
-            if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[(sb + 1) & 1], src, sb + 1);
-            load_raw(rw, src, sb + 1);
+    load_act(st[0], src, cur.k0, tid);
+    if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[0], src, cur.k0, tid);
+    load_raw(rw, src, cur.k0, tid);
+    int ph = 0;   // stage holding the next super-block to compute
+    for (;;) {
+        store_raw(st[ph], rw, tid);
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        Lane L;
+        L.wt = wave & 1;                       // 32-token group of this wave
+        L.hh = lane >> 5;
+        L.ta = 32 * L.wt + (lane & 31);        // token (tile-local) this lane feeds to MFMA a
+        L.jb = 32 * (wave >> 1) + (lane & 31); // weight row (tile-local) of the lane
+        L.l16 = lane & 15;
+        {
+            const int own = 32 * L.ta + 16 * (L.hh ^ swz(L.ta)), zrow = 32 * TT;
+            L.pa0 = L.hh ? zrow : own;
+            L.pa1 = L.hh ? own : zrow;
         }
-
-        // Operand rings, three deep: chunk c+2's MFMA operands and scales are
-        // fetched from LDS while chunk c's epilogue runs.
-        Ab<QT> ab[3];
-        Sc<QT> sc[3];
-        f32x16 xr[2];      // activation scales, loaded one chunk ahead
-        ChunkD<QT> dd[2];
-        load_ab(ab[0], s, 0, L);
-        load_sc(sc[0], s, 0, L);
-        xr[0] = load_x(s, 0, L);
-        MinOp mA, mB;
-        if constexpr (QT == 4 && MODE == 0) {
-            mA = s.ma[L.ta][L.hh];
-            mB = s.mb[L.jb][L.hh];
-        }
-        load_ab(ab[1], s, 1, L);
-        load_sc(sc[1], s, 1, L);
-        dd[0] = mfma_chunk(ab[0], bias);
+        i32x16 bias;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            if (c + 2 < NCH) {
-                load_ab(ab[(c + 2) % 3], s, c + 2, L);
-                load_sc(sc[(c + 2) % 3], s, c + 2, L);
-            }
-            if (c + 1 < NCH) xr[(c + 1) & 1] = load_x(s, c + 1, L);
-            ChunkD<QT> &cur = dd[c & 1];
-            if (c + 1 < NCH) {
-                ChunkD<QT> &nxt = dd[(c + 1) & 1];
-                nxt = mfma_chunk(ab[(c + 1) % 3], bias);
-                pin_after(cur.v[0], nxt.v[QT == 4 ? 0 : 1]);   // issue MFMA c+1 first
-                if constexpr (QT == 6) pin(cur.v[1]);
-            }
-            epilogue<QT, MODE>(cur, sc[c % 3], xr[c & 1], acc, g, tw0, j, sb, c, L);
-            if constexpr (QT == 4 && MODE == 0) {
-                // the super-block's min term: hi*hi, hi*lo, lo*hi
-                if (c == 2) accm = mfma_bf16(mA.w[0], mA.w[1], mB.w[0], mB.w[1], accm);
-                if (c == 4) accm = mfma_bf16(mA.w[0], mA.w[1], mB.w[2], mB.w[3], accm);
-                if (c == 6) accm = mfma_bf16(mA.w[2], mA.w[3], mB.w[0], mB.w[1], accm);
-            }
-            if constexpr (MODE == 0) pin(acc);                  // epilogue c done here
-        }
-        if (more) store_raw(st[(sb + 1) & 1], rw);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int i = 0; i < 16; ++i) bias[i] = MAGIC_I;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the activation copy has landed
         __syncthreads();
-    }
 
-    if constexpr (MODE == 0) {
-        if (j < g.j1) {
+        f32x16 acc, accm;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t t = tw0 + 32 * L.wt + mfma_row(i, L.hh);
-                if (t < g.t1) g.y[t * g.ldy + j] = acc[i] + accm[i];
-            }
+        for (int i = 0; i < 16; ++i) {
+            acc[i] = 0.0f;
+            accm[i] = 0.0f;
         }
+        for (int sb = cur.k0; sb < cur.k1; ++sb) {
+            const Stage<QT> &s = st[ph];
+            Stage<QT> &sn = st[ph ^ 1];
+            const bool more = sb + 1 < cur.k1;
+            if (more) {
+                load_act(sn, src, sb + 1, tid);
+                if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(sn, src, sb + 1, tid);
+                load_raw(rw, src, sb + 1, tid);
+            }
+
+            // Operand rings, three deep: chunk c+2's MFMA operands and scales
+            // are fetched from LDS while chunk c's epilogue runs.
+            Ab<QT> ab[3];
+            Sc<QT> sc[3];
+            f32x16 xr[2];      // activation scales, loaded one chunk ahead
+            ChunkD<QT> dd[2];
+            load_ab(ab[0], s, 0, L);
+            load_sc(sc[0], s, 0, L);
+            xr[0] = load_x(s, 0, L);
+            MinOp mA, mB;
+            if constexpr (QT == 4 && MODE == 0) {
+                mA = s.ma[L.ta][L.hh];
+                mB = s.mb[L.jb][L.hh];
+            }
+            load_ab(ab[1], s, 1, L);
+            load_sc(sc[1], s, 1, L);
+            dd[0] = mfma_chunk(ab[0], bias);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                if (c + 2 < NCH) {
+                    load_ab(ab[(c + 2) % 3], s, c + 2, L);
+                    load_sc(sc[(c + 2) % 3], s, c + 2, L);
+                }
+                if (c + 1 < NCH) xr[(c + 1) & 1] = load_x(s, c + 1, L);
+                ChunkD<QT> &cd = dd[c & 1];
+                if (c + 1 < NCH) {
+                    ChunkD<QT> &nd = dd[(c + 1) & 1];
+                    nd = mfma_chunk(ab[(c + 1) % 3], bias);
+                    pin_after(cd.v[0], nd.v[QT == 4 ? 0 : 1]);   // issue MFMA c+1 first
+                    if constexpr (QT == 6) pin(cd.v[1]);
+                }
+                epilogue<QT, MODE>(cd, sc[c % 3], xr[c & 1], acc, g, tw0, jw0 + L.jb, sb, c, L);
+                if constexpr (QT == 4 && MODE == 0) {
+                    // the super-block's min term: hi*hi, hi*lo, lo*hi
+                    if (c == 2) accm = mfma_bf16(mA.w[0], mA.w[1], mB.w[0], mB.w[1], accm);
+                    if (c == 4) accm = mfma_bf16(mA.w[0], mA.w[1], mB.w[2], mB.w[3], accm);
+                    if (c == 6) accm = mfma_bf16(mA.w[2], mA.w[3], mB.w[0], mB.w[1], accm);
+                }
+                if constexpr (MODE == 0) pin(acc);                  // epilogue c done here
+            }
+            if (more) store_raw(sn, rw, tid);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            ph ^= 1;
+        }
+
+        // Issue the next item's first loads, then finish this tile while they
+        // are in flight.  Its per-lane offsets come from a thread index the
+        // compiler cannot see through, so that they are not hoisted out of
+        // the loop and kept live across the super-block loop.
+        const Work nxt = next_work(g, dpt, it, it_end, G, nsb);
+        if (nxt.k1 != 0) {
+            tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            int64_t nt0, nj0;
+            tile_origin(g, nxt.tile, nt0, nj0);
+            src = make_src<QT, ARM>(g, nt0, nj0, tid);
+            load_act(st[ph], src, nxt.k0, tid);
+            if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[ph], src, nxt.k0, tid);
+            load_raw(rw, src, nxt.k0, tid);
+        }
+        if constexpr (MODE == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] += accm[i];
+            finish_tile(g, acc, cur, v, G, nsb, L, wave, lane);
+        }
+        if (nxt.k1 == 0) break;
+        cur = nxt;
+        tile_origin(g, cur.tile, tw0, jw0);
     }
 }
 
 // ---------------------------------------------------------------------------
 // host-side launchers (argument checking is done by the C ABI layer)
 // ---------------------------------------------------------------------------
+
+// Workgroups that run at once: two per CU.
+static int64_t worker_slots()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MMQ_MAX_WORKERS;
+    if (dev < 0 || dev >= 64) return MMQ_MAX_WORKERS;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return MMQ_MAX_WORKERS;
+        cached[dev] = cus;
+    }
+    return std::min<int64_t>(2 * (int64_t)cached[dev], MMQ_MAX_WORKERS);
+}
+
 template <int QT, int ARM, int MODE>
 static int launch(MmqArgs g, hipStream_t stream)
 {
     const int64_t nbt = (g.t1 - g.t0 + TT - 1) / TT;
     const int64_t nbj = (g.j1 - g.j0 + TJ - 1) / TJ;
     if (nbt <= 0 || nbj <= 0) return 0;
-    if (nbt * nbj > 0x7fffffff) return -1;
+    const int64_t ntiles = nbt * nbj;
+    if (ntiles > 0x7fffffff) return -1;
     g.nbt = (int)nbt;
-    hipLaunchKernelGGL((mmq_kernel<QT, ARM, MODE>), dim3((unsigned)(nbt * nbj)), dim3(NTHR), 0,
-                       stream, g);
+    g.nbj = (int)nbj;
+    // Whole tiles, one per workgroup, unless a workspace is given and the
+    // tiles make one round that leaves a quarter or more of the workgroup
+    // slots (two per CU) empty: then the (tile, super-block) iterations are
+    // shared evenly by all slots (stream-K).  A fuller round, or a shape with
+    // several rounds, measured faster as whole tiles: a second workgroup adds
+    // only about half a CU's throughput, so the CUs left with one workgroup
+    // lose less than the tile count suggests, and each split tile pays a
+    // fix-up of a few microseconds.  (The work list also supports whole-tile
+    // rounds followed by a split remainder: dp_tiles > 0.)
+    int64_t G = ntiles;
+    g.dp_tiles = (int)ntiles;
+    g.sk_tiles = 0;
+    const int64_t nsb = g.id / 256;
+    if (MODE == 0 && g.ws != nullptr && nsb >= 2) {
+        const int64_t S = worker_slots();
+        const int64_t workers = std::min<int64_t>(S, ntiles * nsb / MMQ_MIN_SPLIT_ITERS);
+        if (ntiles * MMQ_SK_FILL_DEN <= S * MMQ_SK_FILL_NUM && workers > ntiles && ntiles * nsb < 0x7fffffff) {
+            g.dp_tiles = 0;
+            g.sk_tiles = (int)ntiles;
+            G = workers;
+        }
+    }
+    hipLaunchKernelGGL((mmq_kernel<QT, ARM, MODE>), dim3((unsigned)G), dim3(NTHR), 0, stream, g);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -686,6 +932,9 @@ int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
     g.j0 = Lc.j0;
     g.j1 = Lc.j1;
     g.nbt = 0;
+    g.nbj = 0;
+    g.ws = static_cast<float *>(Lc.ws);
+    g.cnt = Lc.ws ? reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(Lc.ws) + MMQ_WS_PARTIAL_BYTES) : nullptr;
     const bool part = Lc.P != nullptr;
     if (Lc.qtype == 4) {
         if (Lc.prepared)

@@ -16,7 +16,18 @@ struct MmqLaunch {
     int64_t bstride, od, id, nt, ldy;
     int64_t t0, t1, j0, j1;  // output window
     bool prepared = false;   // W / Wexp point into a prepared buffer
+    void *ws = nullptr;      // stream-K workspace (MMQ_WS_BYTES, zeroed once) or nullptr
 };
+
+// Stream-K workspace: two 64 x 64 fp32 partial-sum slots per worker, then
+// four uint32 arrival counters (one per wave's quarter tile) per worker.  At most MMQ_MAX_WORKERS workers (two
+// per CU); a split needs at least MMQ_MIN_SPLIT_ITERS super-blocks per worker.
+constexpr int64_t MMQ_MAX_WORKERS = 1024;
+constexpr int64_t MMQ_MIN_SPLIT_ITERS = 4;
+// stream-K only for a single round of tiles filling at most NUM/DEN of the slots
+constexpr int64_t MMQ_SK_FILL_NUM = 3, MMQ_SK_FILL_DEN = 4;
+constexpr int64_t MMQ_WS_PARTIAL_BYTES = MMQ_MAX_WORKERS * 2 * 64 * 64 * 4;
+constexpr int64_t MMQ_WS_BYTES = MMQ_WS_PARTIAL_BYTES + MMQ_MAX_WORKERS * 16;
 
 // All return 0, -1 (grid too large) or -3 (launch error).
 int launch_mmq(const MmqLaunch &L, hipStream_t stream);

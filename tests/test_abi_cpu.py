@@ -23,7 +23,9 @@ def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ["quantize_q8_pad40", "mmq_q4k", "mmq_q6k", "expand_q6k_dense", "q8_pad40_bytes",
               "qig_strerror", "mmq_q4k_partials", "mmq_q6k_partials", "q4k_prepared_bytes",
-              "q6k_prepared_bytes", "prepare_q4k", "prepare_q6k", "mmq_q4k_prepared", "mmq_q6k_prepared"]:
+              "q6k_prepared_bytes", "prepare_q4k", "prepare_q6k", "mmq_q4k_prepared", "mmq_q6k_prepared",
+              "mmq_workspace_bytes", "mmq_q4k_streamk", "mmq_q6k_streamk", "mmq_q4k_prepared_streamk",
+              "mmq_q6k_prepared_streamk"]:
         assert n in names
 
 
@@ -140,3 +142,19 @@ def test_prepared_sizes_and_argument_checks():
     assert lib.mmq_q4k_prepared(MIS, 8, 256, B16, 4, A16, 8, None) == -2
     assert lib.mmq_q6k_prepared(A16, 8, 256, B16, 4, A16, 4, None) == -1   # ldy < od
     assert lib.mmq_q6k_prepared(A16, 8, 256, B16, 0, A16, 8, None) == 0    # nt == 0
+
+
+def test_streamk_workspace_and_argument_checks():
+    lib = qig.load()
+    # two 64x64 fp32 partial slots and four counters per workgroup, 1024 workgroups at most
+    assert lib.mmq_workspace_bytes() == 1024 * 2 * 64 * 64 * 4 + 1024 * 16
+    assert lib.mmq_q4k_streamk(A16, 8, 256, B16, 4, A16, 8, None, None) == -1          # no workspace
+    assert lib.mmq_q4k_streamk(A16, 8, 256, B16, 4, A16, 8, MIS, None) == -2           # misaligned workspace
+    assert lib.mmq_q4k_streamk(A16, 8, 300, B16, 4, A16, 8, A16, None) == -1           # id % 256
+    assert lib.mmq_q4k_streamk(A16, 8, 256, B16, 0, A16, 8, A16, None) == 0            # nt == 0
+    assert lib.mmq_q6k_streamk(A16, 208, None, 8, 256, B16, 4, A16, 8, A16, None) == -1   # bstride
+    assert lib.mmq_q6k_streamk(A16, 224, MIS, 8, 256, B16, 4, A16, 8, A16, None) == -2    # W_exp
+    assert lib.mmq_q6k_streamk(A16, 224, None, 8, 256, B16, 4, A16, 8, None, None) == -1
+    assert lib.mmq_q4k_prepared_streamk(A16, 8, 256, B16, 4, A16, 7, A16, None) == -1   # ldy < od
+    assert lib.mmq_q6k_prepared_streamk(A16, 8, 256, B16, 4, A16, 8, MIS, None) == -2
+    assert lib.mmq_q6k_prepared_streamk(A16, 0, 256, B16, 4, A16, 0, A16, None) == 0   # od == 0
