@@ -199,6 +199,50 @@ int mmq_q6k_prepared_streamk(const void *Wp, int64_t od, int64_t id,
                              void *ws, hipStream_t stream);
 
 /*
+ * Tiled activations -- quantization straight into the layout the GEMM stages
+ * (the quantize-transpose prepass the r21 page "Coalesced block-linear A
+ * staging", s5, reports the campaign moving to), so the GEMMs' activation
+ * staging is a plain copy.  The quantization is the pad40 one (same d, quants
+ * and ssum); only the layout differs.  For 64-token tile T = t / 64 and
+ * super-block sb, a record of 20480 bytes at ((T * (id/256)) + sb) * 20480
+ * holds, for its tokens u = t % 64 and chunks c = 0..7 (pad40 chunk
+ * 8 sb + c):
+ *   quants   the 32 int8 of (t, c) at 2048 c + 32 u, each 16-byte half h
+ *            stored at offset 16 (h ^ s(u)), s(u) = ((u >> 2) ^ (u >> 3)) & 1
+ *   d        fp16 d widened to fp32 at 16384 + 256 c + 4 slot(u), slot(u) =
+ *            (u & 32) + 16 ((u >> 2) & 1) + 4 ((u & 31) >> 3) + (u & 3)
+ *   -ssum    split as hi = bf16(-ssum), lo = bf16(-ssum - hi) (round to
+ *            nearest even): 16-byte entry at 18432 + 16 (2 u + c / 4), hi at
+ *            its 16-bit index c % 4, lo at index 4 + c % 4
+ * Tokens nt .. 64 * ceil(nt/64) - 1 are quantized from zeros: d = 0, quants
+ * 0, -ssum = -0 (hi 0x8000, lo 0).  The GEMMs below give y bit-identical to
+ * the pad40 calls of the same name.
+ *
+ *   x      as quantize_q8_pad40; id must be a multiple of 256
+ *   q8t    q8_tiled_bytes(nt, id) = ceil(nt/64) * (id/256) * 20480 bytes,
+ *          16-byte aligned; every byte written
+ *   ws     NULL (whole tiles, as the plain calls) or a stream-K workspace (as
+ *          the *_streamk calls)
+ * Errors: as quantize_q8_pad40 and the GEMM of the same name (QIG_EINVAL also
+ *         for id % 256 in quantize_q8_tiled; QIG_EALIGN for a misaligned ws).
+ */
+size_t q8_tiled_bytes(int64_t nt, int64_t id);
+int quantize_q8_tiled(const float *x, int64_t nt, int64_t id, int64_t ldx,
+                      void *q8t, hipStream_t stream);
+int mmq_q4k_q8t(const void *W, int64_t od, int64_t id, const void *q8t,
+                int64_t nt, float *y, int64_t ldy, void *ws,
+                hipStream_t stream);
+int mmq_q6k_q8t(const void *W, int64_t bstride, const int8_t *W_exp,
+                int64_t od, int64_t id, const void *q8t, int64_t nt, float *y,
+                int64_t ldy, void *ws, hipStream_t stream);
+int mmq_q4k_prepared_q8t(const void *Wp, int64_t od, int64_t id,
+                         const void *q8t, int64_t nt, float *y, int64_t ldy,
+                         void *ws, hipStream_t stream);
+int mmq_q6k_prepared_q8t(const void *Wp, int64_t od, int64_t id,
+                         const void *q8t, int64_t nt, float *y, int64_t ldy,
+                         void *ws, hipStream_t stream);
+
+/*
  * Test exports: the int32 sub-block partials of the same kernels, for the
  * window of tokens [t0, t1) and rows [j0, j1), written to
  * P[(t - t0)][(j - j0)][sub] (int32, 4-byte aligned), where sub runs over all

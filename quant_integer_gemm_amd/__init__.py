@@ -13,18 +13,24 @@ from ._lib import (  # noqa: F401
     mmq_q4k,
     mmq_q4k_partials,
     mmq_q4k_prepared,
+    mmq_q4k_prepared_q8t,
     mmq_q4k_prepared_streamk,
+    mmq_q4k_q8t,
     mmq_q4k_streamk,
     mmq_q6k,
     mmq_q6k_partials,
     mmq_q6k_prepared,
+    mmq_q6k_prepared_q8t,
     mmq_q6k_prepared_streamk,
+    mmq_q6k_q8t,
     mmq_q6k_streamk,
     new_workspace,
     prepare_q4k,
     prepare_q6k,
     prepared_bytes,
     q8_pad40_bytes,
+    q8_tiled_bytes,
     quantize_q8_pad40,
+    quantize_q8_tiled,
     workspace,
 )

@@ -40,6 +40,12 @@ SIGNATURES = {
     "mmq_q6k_streamk": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q4k_prepared_streamk": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q6k_prepared_streamk": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "q8_tiled_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "quantize_q8_tiled": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "mmq_q4k_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "mmq_q6k_q8t": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "mmq_q4k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "mmq_q6k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
 }
 
 
@@ -266,4 +272,60 @@ def mmq_q6k_prepared_streamk(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: in
     ws = workspace(Wp.device) if ws is None else ws
     _check(load().mmq_q6k_prepared_streamk(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"),
                                            ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_prepared_streamk")
+    return y
+
+
+# --- tiled activations (quantization in the GEMM's staging layout) -------------
+
+def q8_tiled_bytes(nt: int, id_: int) -> int:
+    return int(load().q8_tiled_bytes(nt, id_))
+
+
+def quantize_q8_tiled(x, id_: int | None = None, out=None, stream=None):
+    """fp32 x[nt][ldx] (GPU) -> uint8 tiled plane of q8_tiled_bytes(nt, id) bytes."""
+    import torch
+    if x.dim() != 2 or x.dtype != torch.float32 or x.stride(1) != 1:
+        raise QigError("x must be a 2-D fp32 tensor with unit column stride")
+    nt, _ = x.shape
+    id_ = x.shape[1] if id_ is None else id_
+    ldx = x.stride(0) if nt > 1 else max(x.shape[1], id_)
+    if out is None:
+        out = torch.empty(q8_tiled_bytes(nt, id_), dtype=torch.uint8, device=x.device)
+    _check(load().quantize_q8_tiled(_dev_ptr(x, "x"), nt, id_, ldx, _dev_ptr(out, "q8t"), _stream(stream)),
+           "quantize_q8_tiled")
+    return out
+
+
+def mmq_q4k_q8t(W, od: int, id_: int, q8t, nt: int, y=None, ldy: int | None = None, ws=None, stream=None):
+    """mmq_q4k on a tiled activation plane; ws: None (whole tiles) or a stream-K workspace."""
+    y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _check(load().mmq_q4k_q8t(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"), ldy,
+                              _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_q8t")
+    return y
+
+
+def mmq_q6k_q8t(W, bstride: int, od: int, id_: int, q8t, nt: int, W_exp=None, y=None, ldy: int | None = None,
+                ws=None, stream=None):
+    """mmq_q6k on a tiled activation plane; ws: None (whole tiles) or a stream-K workspace."""
+    y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _check(load().mmq_q6k_q8t(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_, _dev_ptr(q8t, "q8t"),
+                              nt, _dev_ptr(y, "y"), ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_q8t")
+    return y
+
+
+def mmq_q4k_prepared_q8t(Wp, od: int, id_: int, q8t, nt: int, y=None, ldy: int | None = None, ws=None,
+                         stream=None):
+    """mmq_q4k_prepared on a tiled activation plane."""
+    y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    _check(load().mmq_q4k_prepared_q8t(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"),
+                                       ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_prepared_q8t")
+    return y
+
+
+def mmq_q6k_prepared_q8t(Wp, od: int, id_: int, q8t, nt: int, y=None, ldy: int | None = None, ws=None,
+                         stream=None):
+    """mmq_q6k_prepared on a tiled activation plane."""
+    y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    _check(load().mmq_q6k_prepared_q8t(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"),
+                                       ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_prepared_q8t")
     return y

@@ -68,39 +68,44 @@ int quantize_q8_pad40(const float *x, int64_t nt, int64_t id, int64_t ldx, void 
     return rc_from_launch(qig::launch_quantize(x, nt, id, ldx, q8, stream));
 }
 
-// ws: the stream-K workspace, or nullptr for whole tiles only.
+// ws: the stream-K workspace, or nullptr for whole tiles only.  tiled: q8 is
+// a tiled plane (quantize_q8_tiled) instead of pad40.
 static int gemm_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
-                    void *ws, hipStream_t stream)
+                    void *ws, bool tiled, hipStream_t stream)
 {
     int rc = check_gemm(W, od, id, q8, nt, y, ldy, 144);
     if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    if (ws && !aligned(ws, 16)) return QIG_EALIGN;
     qig::MmqLaunch L = {4, W, nullptr, q8, y, nullptr, 144, od, id, nt, ldy, 0, nt, 0, od};
     L.ws = ws;
+    L.q8_tiled = tiled;
     return rc_from_launch(qig::launch_mmq(L, stream));
 }
 
 static int gemm_q6k(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id,
-                    const void *q8, int64_t nt, float *y, int64_t ldy, void *ws, hipStream_t stream)
+                    const void *q8, int64_t nt, float *y, int64_t ldy, void *ws, bool tiled, hipStream_t stream)
 {
     if (bad_bstride(bstride)) return QIG_EINVAL;
     int rc = check_gemm(W, od, id, q8, nt, y, ldy, bstride);
     if (rc != QIG_OK || nt == 0 || od == 0) return rc;
     if (W_exp && !aligned(W_exp, 16)) return QIG_EALIGN;
+    if (ws && !aligned(ws, 16)) return QIG_EALIGN;
     qig::MmqLaunch L = {6, W, W_exp, q8, y, nullptr, bstride, od, id, nt, ldy, 0, nt, 0, od};
     L.ws = ws;
+    L.q8_tiled = tiled;
     return rc_from_launch(qig::launch_mmq(L, stream));
 }
 
 int mmq_q4k(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, float *y, int64_t ldy,
             hipStream_t stream)
 {
-    return gemm_q4k(W, od, id, q8, nt, y, ldy, nullptr, stream);
+    return gemm_q4k(W, od, id, q8, nt, y, ldy, nullptr, false, stream);
 }
 
 int mmq_q6k(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id, const void *q8,
             int64_t nt, float *y, int64_t ldy, hipStream_t stream)
 {
-    return gemm_q6k(W, bstride, W_exp, od, id, q8, nt, y, ldy, nullptr, stream);
+    return gemm_q6k(W, bstride, W_exp, od, id, q8, nt, y, ldy, nullptr, false, stream);
 }
 
 size_t mmq_workspace_bytes(void) { return (size_t)qig::MMQ_WS_BYTES; }
@@ -110,7 +115,7 @@ int mmq_q4k_streamk(const void *W, int64_t od, int64_t id, const void *q8, int64
 {
     if (!ws) return QIG_EINVAL;
     if (!aligned(ws, 16)) return QIG_EALIGN;
-    return gemm_q4k(W, od, id, q8, nt, y, ldy, ws, stream);
+    return gemm_q4k(W, od, id, q8, nt, y, ldy, ws, false, stream);
 }
 
 int mmq_q6k_streamk(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id,
@@ -118,7 +123,7 @@ int mmq_q6k_streamk(const void *W, int64_t bstride, const int8_t *W_exp, int64_t
 {
     if (!ws) return QIG_EINVAL;
     if (!aligned(ws, 16)) return QIG_EALIGN;
-    return gemm_q6k(W, bstride, W_exp, od, id, q8, nt, y, ldy, ws, stream);
+    return gemm_q6k(W, bstride, W_exp, od, id, q8, nt, y, ldy, ws, false, stream);
 }
 
 int expand_q6k_dense(const void *W, int64_t bstride, int64_t od, int64_t id, int8_t *W_exp,
@@ -169,14 +174,16 @@ int prepare_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, void *Wp
 }
 
 static int mmq_prepared(int qtype, const void *Wp, int64_t od, int64_t id, const void *q8, int64_t nt, float *y,
-                        int64_t ldy, void *ws, hipStream_t stream)
+                        int64_t ldy, void *ws, hipStream_t stream, bool tiled = false)
 {
     int rc = check_gemm(Wp, od, id, q8, nt, y, ldy, 64);
     if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    if (ws && !aligned(ws, 16)) return QIG_EALIGN;
     const int8_t *Q = static_cast<const int8_t *>(Wp);
     const void *S = static_cast<const uint8_t *>(Wp) + prepared_quant_bytes(qtype, od, id);
     qig::MmqLaunch L = {qtype, S, Q, q8, y, nullptr, 64, od, id, nt, ldy, 0, nt, 0, od, true};
     L.ws = ws;
+    L.q8_tiled = tiled;
     return rc_from_launch(qig::launch_mmq(L, stream));
 }
 
@@ -206,6 +213,45 @@ int mmq_q6k_prepared_streamk(const void *Wp, int64_t od, int64_t id, const void 
     if (!ws) return QIG_EINVAL;
     if (!aligned(ws, 16)) return QIG_EALIGN;
     return mmq_prepared(6, Wp, od, id, q8, nt, y, ldy, ws, stream);
+}
+
+size_t q8_tiled_bytes(int64_t nt, int64_t id)
+{
+    if (nt < 0 || id <= 0 || id % 256 != 0) return 0;
+    return (size_t)((nt + 63) / 64) * (size_t)(id / 256) * (size_t)qig::Q8T_RECORD;
+}
+
+int quantize_q8_tiled(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q8t, hipStream_t stream)
+{
+    if (nt < 0 || id <= 0 || id % 256 != 0 || ldx < id) return QIG_EINVAL;
+    if (nt == 0) return QIG_OK;
+    if (!x || !q8t) return QIG_EINVAL;
+    if (!aligned(x, 16) || !aligned(q8t, 16) || ldx % 4 != 0) return QIG_EALIGN;
+    return rc_from_launch(qig::launch_quantize_tiled(x, nt, id, ldx, q8t, stream));
+}
+
+int mmq_q4k_q8t(const void *W, int64_t od, int64_t id, const void *q8t, int64_t nt, float *y, int64_t ldy, void *ws,
+                hipStream_t stream)
+{
+    return gemm_q4k(W, od, id, q8t, nt, y, ldy, ws, true, stream);
+}
+
+int mmq_q6k_q8t(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id, const void *q8t,
+                int64_t nt, float *y, int64_t ldy, void *ws, hipStream_t stream)
+{
+    return gemm_q6k(W, bstride, W_exp, od, id, q8t, nt, y, ldy, ws, true, stream);
+}
+
+int mmq_q4k_prepared_q8t(const void *Wp, int64_t od, int64_t id, const void *q8t, int64_t nt, float *y, int64_t ldy,
+                         void *ws, hipStream_t stream)
+{
+    return mmq_prepared(4, Wp, od, id, q8t, nt, y, ldy, ws, stream, true);
+}
+
+int mmq_q6k_prepared_q8t(const void *Wp, int64_t od, int64_t id, const void *q8t, int64_t nt, float *y, int64_t ldy,
+                         void *ws, hipStream_t stream)
+{
+    return mmq_prepared(6, Wp, od, id, q8t, nt, y, ldy, ws, stream, true);
 }
 
 int mmq_q4k_partials(const void *W, int64_t od, int64_t id, const void *q8, int64_t nt, int64_t t0,

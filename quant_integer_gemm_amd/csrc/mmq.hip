@@ -40,6 +40,7 @@
 //    numbered in groups of 8 row tiles and workers XCD by XCD, so the tiles
 //    running on one XCD at a time share operands in its L2.
 #include <algorithm>
+#include <cstddef>
 #include <utility>
 
 #include "qig_device.h"
@@ -60,6 +61,12 @@ constexpr int NCH = 8;    // 32-element chunks per super-block
 // or split from packed nibbles as in RAW (q4_K, whose nibble plane moves
 // half the bytes of a byte plane).
 constexpr int ARM_RAW = 0, ARM_WEXP = 1, ARM_PREP = 2;
+
+// Activation sources.  PAD40: the pad40 plane; quants are copied into LDS,
+// d and ssum go through registers (d widened, -ssum split into bf16 pairs).
+// TILED: the tiled plane of quantize_q8_tiled, whose records already hold
+// the LDS image of all three, so the whole activation stage is a copy.
+constexpr int ACT_PAD40 = 0, ACT_TILED = 1;
 
 // One super-block of staged operands.
 template <int QT>
@@ -90,6 +97,10 @@ struct Stage<4> {
     MinOp mb[TJ][2];            // dmin * m of row j, chunks 4h .. 4h+3
 };
 
+static_assert(offsetof(Stage<4>, ax) == 16384 && offsetof(Stage<4>, ma) == 18432 &&
+                  offsetof(Stage<4>, b) == Q8T_RECORD,
+              "the tiled activation record is the byte image of the first Q8T_RECORD bytes of Stage<4>");
+
 // q6_K: row TT of every chunk plane of a is all zero.  Each 16-element
 // sub-block has its own MFMA, which must see zeros in the lanes that carry
 // the other half of the chunk; those lanes read the zero row instead of
@@ -102,16 +113,6 @@ struct Stage<6> {
     float bs[NCH][TJ][2];       // d * sc of the two 16-element sub-blocks
 };
 
-// Position of tile token t in a row of ax: within each 32-token group the
-// tokens are ordered as the rows of the MFMA result registers, so the 16 rows
-// lane half hh holds are 16 consecutive floats (mfma_row(i, hh) -> 16*hh + i).
-__device__ __forceinline__ int x_slot(int t) { return (t & 32) + row_slot(t & 31); }
-
-// The 16-byte half h of row r is stored at half h ^ swz(r).  An LDS access
-// phase serves 8 (32 banks) or 16 (64 banks) lanes reading 16 bytes of
-// consecutive rows 32 bytes apart; flipping the half on bit 2 xor bit 3 of
-// the row spreads both kinds of phase over distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 struct MmqArgs {
     const uint8_t *W;
@@ -151,14 +152,6 @@ __device__ __forceinline__ void pin(T &x) { asm volatile("" : "+v"(x)); }
 template <typename T, typename U>
 __device__ __forceinline__ void pin_after(T &x, const U &y) { asm volatile("" : "+v"(x) : "v"(y)); }
 
-// v = hi + lo + O(2^-16 v) with hi, lo bf16 (round to nearest even).
-__device__ __forceinline__ void bf16_split(float v, uint16_t &hi, uint16_t &lo)
-{
-    const __bf16 h = (__bf16)v;
-    const __bf16 l = (__bf16)(v - (float)h);
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = __builtin_bit_cast(uint16_t, l);
-}
 
 // ---------------------------------------------------------------------------
 // Staging.  Activations are copied straight into LDS (make_src, load_act).
@@ -201,7 +194,7 @@ struct Src {
     int64_t wstep;       // bytes per super-block along w
 };
 
-template <int QT, int ARM>
+template <int QT, int ARM, int ACT>
 __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t jw0, int tid)
 {
     Src s;
@@ -215,8 +208,14 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
     // 2w+1), chunk l/8: eight tokens of one chunk per lane octet, which keeps
     // their LDS stores (store_raw) free of conflicts.
     const uint32_t tok = (uint32_t)(nb32 * 40);      // bytes per token
-    s.q8 = g.q8 + tw0 * (int64_t)tok;
-    {
+    if constexpr (ACT == ACT_TILED) {
+        // the tile's records (tiles start at multiples of 64 tokens); lane l
+        // copies bytes 16 l .. 16 l + 15 of every 1 KB piece
+        s.q8 = g.q8 + (tw0 / 64) * nsb * Q8T_RECORD;
+        s.aq[0] = s.aq[1] = 16u * (uint32_t)(tid & 63);
+        s.ad[0] = s.ad[1] = 0;
+    } else {
+        s.q8 = g.q8 + tw0 * (int64_t)tok;
         const int l = tid & 63, w = tid >> 6;
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
@@ -305,6 +304,41 @@ __device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb
     }
 }
 
+// Tiled activations: the record of super-block sb holds the first
+// Q8T_RECORD bytes of the q4_K stage (quants, d table, min-term operands)
+// byte for byte; q6_K takes the quants, into its chunk planes (which keep a
+// zero row after each), and the d table.  NP pieces of 1 KB, spread over the
+// four waves.
+template <int QT>
+__device__ __forceinline__ void load_act_tiled(Stage<QT> &st, const Src &s, int64_t sb, int tid)
+{
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    constexpr int NP = QT == 4 ? 20 : 18;
+    const uint8_t *rec = s.q8 + sb * Q8T_RECORD;
+#pragma unroll
+    for (int i = 0; i < (NP + 3) / 4; ++i) {
+        const int p = w + 4 * i;
+        if (p < NP) {
+            uint8_t *dst;
+            if constexpr (QT == 4)
+                dst = reinterpret_cast<uint8_t *>(&st) + 1024 * p;
+            else
+                dst = p < 16 ? &st.a[p >> 1][32 * (p & 1)][0]
+                             : reinterpret_cast<uint8_t *>(&st.ax[0][0]) + 1024 * (p - 16);
+            dma16(rec + 1024 * p, s.aq[0], dst);
+        }
+    }
+}
+
+template <int QT, int ACT>
+__device__ __forceinline__ void stage_act(Stage<QT> &st, const Src &s, int64_t sb, int tid)
+{
+    if constexpr (ACT == ACT_TILED)
+        load_act_tiled(st, s, sb, tid);
+    else
+        load_act(st, s, sb, tid);
+}
+
 // Dense arms: direct global->LDS copies of super-block sb's quants from the
 // quant plane into stage b (same completion rule as load_act).
 template <int QT>
@@ -319,16 +353,18 @@ __device__ __forceinline__ void load_wexp(Stage<QT> &st, const Src &s, int64_t s
     }
 }
 
-template <int QT, int ARM>
+template <int QT, int ARM, int ACT>
 __device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t sb, int tid)
 {
     const int part = (tid >> 4) & 3;
-    const uint8_t *q8 = s.q8 + sb * 320;
-    r.ad[0] = *reinterpret_cast<const uint32_t *>(q8 + s.ad[0]);
-    r.ad[1] = *reinterpret_cast<const uint32_t *>(q8 + s.ad[1]);
-    if constexpr (QT == 4) {
-        r.as[0] = *reinterpret_cast<const uint32_t *>(q8 + 36 + s.ad[0]);
-        r.as[1] = *reinterpret_cast<const uint32_t *>(q8 + 36 + s.ad[1]);
+    if constexpr (ACT == ACT_PAD40) {
+        const uint8_t *q8 = s.q8 + sb * 320;
+        r.ad[0] = *reinterpret_cast<const uint32_t *>(q8 + s.ad[0]);
+        r.ad[1] = *reinterpret_cast<const uint32_t *>(q8 + s.ad[1]);
+        if constexpr (QT == 4) {
+            r.as[0] = *reinterpret_cast<const uint32_t *>(q8 + 36 + s.ad[0]);
+            r.as[1] = *reinterpret_cast<const uint32_t *>(q8 + 36 + s.ad[1]);
+        }
     }
     const uint8_t *blk = s.w + sb * s.wstep + s.wo;
     if constexpr (ARM == ARM_PREP) {
@@ -355,13 +391,13 @@ __device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t 
     }
 }
 
-template <int QT, int ARM>
+template <int QT, int ARM, int ACT>
 __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r, int tid)
 {
     const int row = 16 * (tid >> 6) + (tid & 15), part = (tid >> 4) & 3;
     const int sw = swz(row);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < (ACT == ACT_PAD40 ? 2 : 0); ++i) {
         const int l = tid & 63, t = 8 * (2 * (tid >> 6) + i) + (l & 7);
         s.ax[l >> 3][x_slot(t)] = h2f(r.ad[i]);
         if constexpr (QT == 4) {
@@ -712,7 +748,7 @@ __device__ __forceinline__ void finish_tile(const MmqArgs &g, const f32x16 &p, c
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int QT, int ARM, int MODE>
+template <int QT, int ARM, int MODE, int ACT>
 __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 {
     __shared__ Stage<QT> st[2];
@@ -743,14 +779,14 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     asm volatile("" : "+v"(tid));
     int64_t tw0, jw0;
     tile_origin(g, cur.tile, tw0, jw0);
-    Src src = make_src<QT, ARM>(g, tw0, jw0, tid);
+    Src src = make_src<QT, ARM, ACT>(g, tw0, jw0, tid);
     Raw<QT, ARM> rw;
-    load_act(st[0], src, cur.k0, tid);
+    stage_act<QT, ACT>(st[0], src, cur.k0, tid);
     if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[0], src, cur.k0, tid);
-    load_raw(rw, src, cur.k0, tid);
+    load_raw<QT, ARM, ACT>(rw, src, cur.k0, tid);
     int ph = 0;   // stage holding the next super-block to compute
     for (;;) {
-        store_raw(st[ph], rw, tid);
+        store_raw<QT, ARM, ACT>(st[ph], rw, tid);
         const int lane = tid & 63;
         const int wave = tid >> 6;
         Lane L;
@@ -781,9 +817,9 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             Stage<QT> &sn = st[ph ^ 1];
             const bool more = sb + 1 < cur.k1;
             if (more) {
-                load_act(sn, src, sb + 1, tid);
+                stage_act<QT, ACT>(sn, src, sb + 1, tid);
                 if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(sn, src, sb + 1, tid);
-                load_raw(rw, src, sb + 1, tid);
+                load_raw<QT, ARM, ACT>(rw, src, sb + 1, tid);
             }
 
             // Operand rings, three deep: chunk c+2's MFMA operands and scales
@@ -826,7 +862,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
                 }
                 if constexpr (MODE == 0) pin(acc);                  // epilogue c done here
             }
-            if (more) store_raw(sn, rw, tid);
+            if (more) store_raw<QT, ARM, ACT>(sn, rw, tid);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             ph ^= 1;
@@ -842,10 +878,10 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             asm volatile("" : "+v"(tid));
             int64_t nt0, nj0;
             tile_origin(g, nxt.tile, nt0, nj0);
-            src = make_src<QT, ARM>(g, nt0, nj0, tid);
-            load_act(st[ph], src, nxt.k0, tid);
+            src = make_src<QT, ARM, ACT>(g, nt0, nj0, tid);
+            stage_act<QT, ACT>(st[ph], src, nxt.k0, tid);
             if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[ph], src, nxt.k0, tid);
-            load_raw(rw, src, nxt.k0, tid);
+            load_raw<QT, ARM, ACT>(rw, src, nxt.k0, tid);
         }
         if constexpr (MODE == 0) {
 #pragma unroll
@@ -878,7 +914,7 @@ static int64_t worker_slots()
     return std::min<int64_t>(2 * (int64_t)cached[dev], MMQ_MAX_WORKERS);
 }
 
-template <int QT, int ARM, int MODE>
+template <int QT, int ARM, int MODE, int ACT = ACT_PAD40>
 static int launch(MmqArgs g, hipStream_t stream)
 {
     const int64_t nbt = (g.t1 - g.t0 + TT - 1) / TT;
@@ -910,7 +946,7 @@ static int launch(MmqArgs g, hipStream_t stream)
             G = workers;
         }
     }
-    hipLaunchKernelGGL((mmq_kernel<QT, ARM, MODE>), dim3((unsigned)G), dim3(NTHR), 0, stream, g);
+    hipLaunchKernelGGL((mmq_kernel<QT, ARM, MODE, ACT>), dim3((unsigned)G), dim3(NTHR), 0, stream, g);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -936,6 +972,14 @@ int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
     g.ws = static_cast<float *>(Lc.ws);
     g.cnt = Lc.ws ? reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(Lc.ws) + MMQ_WS_PARTIAL_BYTES) : nullptr;
     const bool part = Lc.P != nullptr;
+    if (Lc.q8_tiled) {
+        // whole-output GEMMs only (the partials exports read pad40)
+        if (part) return -1;
+        if (Lc.qtype == 4)
+            return Lc.prepared ? launch<4, ARM_PREP, 0, ACT_TILED>(g, stream) : launch<4, ARM_RAW, 0, ACT_TILED>(g, stream);
+        if (Lc.prepared) return launch<6, ARM_PREP, 0, ACT_TILED>(g, stream);
+        return Lc.Wexp ? launch<6, ARM_WEXP, 0, ACT_TILED>(g, stream) : launch<6, ARM_RAW, 0, ACT_TILED>(g, stream);
+    }
     if (Lc.qtype == 4) {
         if (Lc.prepared)
             return part ? launch<4, ARM_PREP, 1>(g, stream) : launch<4, ARM_PREP, 0>(g, stream);

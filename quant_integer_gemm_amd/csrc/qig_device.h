@@ -75,6 +75,27 @@ __device__ __forceinline__ int row_slot(int tau)
     return 16 * ((tau >> 2) & 1) + 4 * (tau >> 3) + (tau & 3);
 }
 
+// Position of tile token t (0..63) in a row of a per-token scale table: each
+// 32-token group in register order, so the 16 rows a lane half holds are 16
+// consecutive entries.
+__device__ __forceinline__ int x_slot(int t) { return (t & 32) + row_slot(t & 31); }
+
+// The 16-byte half h of quant row r (32 bytes) is stored at half h ^ swz(r).
+// An LDS access phase serves 8 (32 banks) or 16 (64 banks) lanes reading 16
+// bytes of consecutive rows 32 bytes apart; flipping the half on bit 2 xor
+// bit 3 of the row spreads both kinds of phase over distinct 16-byte bank
+// groups.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+// v = hi + lo + O(2^-16 v) with hi, lo bf16 (round to nearest even).
+__device__ __forceinline__ void bf16_split(float v, uint16_t &hi, uint16_t &lo)
+{
+    const __bf16 h = (__bf16)v;
+    const __bf16 l = (__bf16)(v - (float)h);
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, l);
+}
+
 // Four 6-bit values v in [0, 63], one per byte, to the two's-complement
 // bytes of v - 32: v + 0x60 stays below 0x100 (no carry between bytes) and
 // flipping bit 7 then gives v - 32 modulo 256.

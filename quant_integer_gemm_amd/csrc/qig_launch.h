@@ -17,6 +17,7 @@ struct MmqLaunch {
     int64_t t0, t1, j0, j1;  // output window
     bool prepared = false;   // W / Wexp point into a prepared buffer
     void *ws = nullptr;      // stream-K workspace (MMQ_WS_BYTES, zeroed once) or nullptr
+    bool q8_tiled = false;   // q8 is a tiled plane (launch_quantize_tiled), not pad40
 };
 
 // Stream-K workspace: two 64 x 64 fp32 partial-sum slots per worker, then
@@ -35,6 +36,12 @@ int launch_quantize(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q
                     hipStream_t stream);
 int launch_expand_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, int8_t *Wexp,
                       hipStream_t stream);
+// Tiled activation plane: one record of Q8T_RECORD bytes per (64-token tile,
+// super-block) -- quants [8][64][32] (halves swizzled), fp32 d [8][64] in
+// register order, bf16 hi/lo pairs of -ssum [64][2][8] -- the first bytes of
+// the GEMM's LDS stage, so the GEMM copies it without conversion.
+constexpr int64_t Q8T_RECORD = 20480;
+int launch_quantize_tiled(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q8t, hipStream_t stream);
 // Prepared buffers: quant plane (q6_K: [od][id] centred int8; q4_K:
 // [od][id/2] packed nibble bytes), then scale plane [od][id/256][16] fp32
 // (q4_K: d*sc and dmin*m of each of the 8 sub-blocks, in pairs; q6_K: d*sc

@@ -25,7 +25,8 @@ def test_header_declares_expected_entry_points():
               "qig_strerror", "mmq_q4k_partials", "mmq_q6k_partials", "q4k_prepared_bytes",
               "q6k_prepared_bytes", "prepare_q4k", "prepare_q6k", "mmq_q4k_prepared", "mmq_q6k_prepared",
               "mmq_workspace_bytes", "mmq_q4k_streamk", "mmq_q6k_streamk", "mmq_q4k_prepared_streamk",
-              "mmq_q6k_prepared_streamk"]:
+              "mmq_q6k_prepared_streamk", "q8_tiled_bytes", "quantize_q8_tiled", "mmq_q4k_q8t", "mmq_q6k_q8t",
+              "mmq_q4k_prepared_q8t", "mmq_q6k_prepared_q8t"]:
         assert n in names
 
 
@@ -158,3 +159,23 @@ def test_streamk_workspace_and_argument_checks():
     assert lib.mmq_q4k_prepared_streamk(A16, 8, 256, B16, 4, A16, 7, A16, None) == -1   # ldy < od
     assert lib.mmq_q6k_prepared_streamk(A16, 8, 256, B16, 4, A16, 8, MIS, None) == -2
     assert lib.mmq_q6k_prepared_streamk(A16, 0, 256, B16, 4, A16, 0, A16, None) == 0   # od == 0
+
+
+def test_tiled_sizes_and_argument_checks():
+    lib = qig.load()
+    assert qig.q8_tiled_bytes(512, 3584) == 8 * 14 * 20480 == qig.q8_pad40_bytes(512, 3584)
+    assert qig.q8_tiled_bytes(70, 768) == 2 * 3 * 20480
+    assert qig.q8_tiled_bytes(0, 256) == 0
+    assert qig.q8_tiled_bytes(5, 100) == 0 and qig.q8_tiled_bytes(5, 288) == 0   # id % 256
+    assert lib.quantize_q8_tiled(A16, 4, 288, 288, B16, None) == -1      # id % 256
+    assert lib.quantize_q8_tiled(A16, 4, 256, 128, B16, None) == -1      # ldx < id
+    assert lib.quantize_q8_tiled(MIS, 4, 256, 256, B16, None) == -2
+    assert lib.quantize_q8_tiled(A16, 4, 256, 258, B16, None) == -2      # ldx % 4
+    assert lib.quantize_q8_tiled(A16, 0, 256, 256, B16, None) == 0
+    assert lib.mmq_q4k_q8t(A16, 8, 300, B16, 4, A16, 8, None, None) == -1
+    assert lib.mmq_q4k_q8t(A16, 8, 256, B16, 4, A16, 8, MIS, None) == -2    # misaligned workspace
+    assert lib.mmq_q4k_q8t(A16, 8, 256, B16, 0, A16, 8, None, None) == 0
+    assert lib.mmq_q6k_q8t(A16, 208, None, 8, 256, B16, 4, A16, 8, None, None) == -1
+    assert lib.mmq_q6k_q8t(A16, 224, MIS, 8, 256, B16, 4, A16, 8, None, None) == -2
+    assert lib.mmq_q4k_prepared_q8t(A16, 8, 256, B16, 4, A16, 7, None, None) == -1   # ldy < od
+    assert lib.mmq_q6k_prepared_q8t(MIS, 8, 256, B16, 4, A16, 8, None, None) == -2

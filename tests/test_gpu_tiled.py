@@ -1,0 +1,161 @@
+"""GPU parity of the tiled activation plane (quantization in the GEMM's
+staging layout) and of the GEMMs that read it.
+
+Bars: the tiled plane bit-exact against the oracle's pad40 quantization laid
+out as the C header documents (quants with swizzled halves, fp32 d in
+register order, -ssum split into bf16 hi + lo); every GEMM on the tiled plane
+bit-identical to the same GEMM on the pad40 plane (whole tiles and stream-K),
+and within the output tolerance of the oracle on small shapes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quant_integer_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+REC = 20480
+
+
+@pytest.fixture(scope="module")
+def qig():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import quant_integer_gemm_amd as q
+    q.load()
+    return q
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _bf16_rne(v):
+    """float32 array -> bf16 bits (round to nearest even), as uint32 in the low half."""
+    u = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
+
+
+def _tiled_expected(q8, nt, id_):
+    """The tiled plane from a pad40 plane, per the layout the header states."""
+    nb32, nsb, ntt = id_ // 32, id_ // 256, (nt + 63) // 64
+    blk = np.zeros((ntt * 64, nb32, 40), dtype=np.uint8)
+    blk[:nt] = q8.reshape(nt, nb32, 40)                  # padding tokens: quantized zeros
+    d = blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float32)
+    qs = blk[:, :, 4:36]
+    ssum = blk[:, :, 36:40].copy().view(np.float32)[:, :, 0]
+    out = np.zeros((ntt, nsb, REC), dtype=np.uint8)
+    u = np.arange(64)
+    s = ((u >> 2) ^ (u >> 3)) & 1
+    slot = (u & 32) + 16 * ((u >> 2) & 1) + 4 * ((u & 31) >> 3) + (u & 3)
+    for T in range(ntt):
+        tok = slice(64 * T, 64 * T + 64)
+        for sb in range(nsb):
+            rec = out[T, sb]
+            for c in range(8):
+                ch = 8 * sb + c
+                rows = qs[tok, ch]                                    # [64][32]
+                for h in range(2):
+                    base = 2048 * c + 32 * u + 16 * (h ^ s)
+                    idx = base[:, None] + np.arange(16)[None, :]
+                    rec[idx] = rows[:, 16 * h:16 * h + 16]
+                dv = np.zeros(64, dtype=np.float32)
+                dv[slot] = d[tok, ch]
+                rec[16384 + 256 * c:16384 + 256 * c + 256] = dv.view(np.uint8)
+                v = (-ssum[tok, ch]).astype(np.float32)
+                hi = _bf16_rne(v)
+                lo = _bf16_rne(v - (hi << 16).astype(np.uint32).view(np.float32))
+                m = rec[18432:20480].view(np.uint16).reshape(64, 2, 8)
+                m[:, c // 4, c % 4] = hi.astype(np.uint16)
+                m[:, c // 4, 4 + c % 4] = lo.astype(np.uint16)
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("nt,id_,kind", [(16, 512, "normal"), (70, 768, "zeros"), (1, 256, "normal"),
+                                         (129, 2304, "tiny"), (512, 3584, "normal"), (300, 18944, "heavy")])
+def test_tiled_plane_bit_exact(qig, nt, id_, kind):
+    g = inputs.rng(4000 + nt + id_)
+    x = g.standard_normal((nt, id_), dtype=np.float32)
+    if kind == "zeros":
+        x[::3, :96] = 0.0
+    elif kind == "tiny":
+        x *= np.float32(1e-6)
+    elif kind == "heavy":
+        x = (g.standard_t(2.0, size=(nt, id_)) * 3).astype(np.float32)
+    want = _tiled_expected(oracle.quantize_q8_pad40(x), nt, id_)
+    got = host(qig.quantize_q8_tiled(dev(x)))
+    assert got.size == qig.q8_tiled_bytes(nt, id_) == want.size
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]} (record offsets {bad[:8] % REC})"
+
+
+def test_tiled_plane_row_stride(qig):
+    g = inputs.rng(4100)
+    x = g.standard_normal((37, 800), dtype=np.float32)
+    want = _tiled_expected(oracle.quantize_q8_pad40(x, id_=768), 37, 768)
+    got = host(qig.quantize_q8_tiled(dev(x), id_=768))
+    assert np.array_equal(got, want)
+
+
+ARMS = ["q4_K", "q4_K_prepared", "q6_K", "q6_K_wexp", "q6_K_prepared"]
+
+
+def _gemm_pair(qig, arm, W, od, id_, q8d, q8td, nt, ws=None):
+    """(y on pad40, y on the tiled plane) for one arm; ws: None or a stream-K workspace."""
+    Wd = dev(W)
+    if arm == "q4_K":
+        a = qig.mmq_q4k_streamk(Wd, od, id_, q8d, nt, ws=ws) if ws is not None else qig.mmq_q4k(Wd, od, id_, q8d, nt)
+        b = qig.mmq_q4k_q8t(Wd, od, id_, q8td, nt, ws=ws)
+    elif arm in ("q6_K", "q6_K_wexp"):
+        We = qig.expand_q6k_dense(Wd, 224, od, id_) if arm == "q6_K_wexp" else None
+        a = (qig.mmq_q6k_streamk(Wd, 224, od, id_, q8d, nt, W_exp=We, ws=ws) if ws is not None
+             else qig.mmq_q6k(Wd, 224, od, id_, q8d, nt, W_exp=We))
+        b = qig.mmq_q6k_q8t(Wd, 224, od, id_, q8td, nt, W_exp=We, ws=ws)
+    elif arm == "q4_K_prepared":
+        Wp = qig.prepare_q4k(Wd, od, id_)
+        a = (qig.mmq_q4k_prepared_streamk(Wp, od, id_, q8d, nt, ws=ws) if ws is not None
+             else qig.mmq_q4k_prepared(Wp, od, id_, q8d, nt))
+        b = qig.mmq_q4k_prepared_q8t(Wp, od, id_, q8td, nt, ws=ws)
+    else:
+        Wp = qig.prepare_q6k(Wd, 224, od, id_)
+        a = (qig.mmq_q6k_prepared_streamk(Wp, od, id_, q8d, nt, ws=ws) if ws is not None
+             else qig.mmq_q6k_prepared(Wp, od, id_, q8d, nt))
+        b = qig.mmq_q6k_prepared_q8t(Wp, od, id_, q8td, nt, ws=ws)
+    return host(a), host(b)
+
+
+@pytest.mark.parametrize("arm", ARMS)
+@pytest.mark.parametrize("nt,od,id_", [(16, 256, 512), (70, 130, 768), (129, 257, 512), (1, 1, 256),
+                                       (512, 3584, 3584)])
+def test_tiled_gemm_matches_pad40_bitwise(qig, arm, nt, od, id_):
+    gm = inputs.Gemm("t", arm[:4], od, id_, nt)
+    W, x = inputs.make_gemm_inputs(gm, inputs.SEED_BASE + 1100 + nt + od)
+    xd = dev(x)
+    y_pad, y_til = _gemm_pair(qig, arm, W, od, id_, qig.quantize_q8_pad40(xd), qig.quantize_q8_tiled(xd), nt)
+    assert np.array_equal(y_til.view(np.uint32), y_pad.view(np.uint32))
+    if nt * od <= 129 * 257:
+        q8 = oracle.quantize_q8_pad40(x)
+        ref = oracle.mmq_q4k(W, od, id_, q8, nt) if arm.startswith("q4") else oracle.mmq_q6k(W, 224, od, id_, q8, nt)
+        ok, worst = oracle.within_tolerance(y_til, ref)
+        assert ok, f"{arm} {nt}x{od}x{id_}: worst error/allowance = {worst:.3g}"
+
+
+@pytest.mark.parametrize("arm", ARMS)
+@pytest.mark.parametrize("nt,od,id_", [(100, 200, 2048), (64, 64, 10240), (2630, 512, 3584)])
+def test_tiled_gemm_streamk_matches_pad40_bitwise(qig, arm, nt, od, id_):
+    """Split tiles: the same decomposition and fix-up order on both planes."""
+    gm = inputs.Gemm("t", arm[:4], od, id_, nt)
+    W, x = inputs.make_gemm_inputs(gm, inputs.SEED_BASE + 1200 + nt + od)
+    xd = dev(x)
+    ws = qig.new_workspace("cuda")
+    y_pad, y_til = _gemm_pair(qig, arm, W, od, id_, qig.quantize_q8_pad40(xd), qig.quantize_q8_tiled(xd), nt,
+                              ws=ws)
+    assert np.array_equal(y_til.view(np.uint32), y_pad.view(np.uint32))
+    assert int(torch.count_nonzero(ws[-16384:]).item()) == 0
