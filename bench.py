@@ -3,9 +3,13 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input at
 the q-projection shape (od = id = 3584, nt = 512):
-    quantize_q8_pad40(x4) -> mmq_q4k(W4)            (q4_K GEMM)
-    quantize_q8_pad40(x6) -> mmq_q6k(W6)            (q6_K GEMM, raw blocks)
-                          -> mmq_q6k(W6, W_exp)     (q6_K GEMM, dense-plane arm)
+    quantize(x4) -> q4_K GEMM (W4)
+    quantize(x6) -> q6_K GEMM (W6, raw blocks)
+                 -> q6_K GEMM (W6, dense-plane arm)
+With --activations tiled (the default) the quantization writes the tiled
+plane (quantize_q8_tiled) and the GEMMs are the *_q8t calls; with pad40 it is
+quantize_q8_pad40 and mmq_q4k / mmq_q6k.  Both give bit-identical y; the
+other form's step is timed too and reported beside the main value.
 Inputs are resident in HBM before timing; the dense plane is built once
 beforehand (it is registration-time work) and timed separately, as are the
 prepared-buffer GEMMs (registration-time quant + fp32 scale planes), which are
@@ -40,8 +44,12 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # about 40 ms of steps: a shorter warmup leaves the GPU below its steady
+    # clocks and measured up to ~10% slow, depending on what ran first
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--activations", choices=["tiled", "pad40"], default="tiled",
+                   help="activation plane of the timed step (the other form is timed and reported too)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy 3x (outside the timed region) so that "
                         "HBM counters taken over this run can be scaled by a kernel of known traffic")
@@ -123,6 +131,8 @@ def main():
     nb = qig.q8_pad40_bytes(NT, ID)
     q84 = torch.empty(nb, dtype=torch.uint8, device=dev)
     q86 = torch.empty(nb, dtype=torch.uint8, device=dev)
+    t84 = torch.empty(qig.q8_tiled_bytes(NT, ID), dtype=torch.uint8, device=dev)
+    t86 = torch.empty(qig.q8_tiled_bytes(NT, ID), dtype=torch.uint8, device=dev)
     y4 = torch.empty((NT, OD), dtype=torch.float32, device=dev)
     y6 = torch.empty((NT, OD), dtype=torch.float32, device=dev)
     y6e = torch.empty((NT, OD), dtype=torch.float32, device=dev)
@@ -150,14 +160,26 @@ def main():
     y4p = torch.empty((NT, OD), dtype=torch.float32, device=dev)
     y6p = torch.empty((NT, OD), dtype=torch.float32, device=dev)
 
-    names = ["quantize_x4", "mmq_q4k", "quantize_x6", "mmq_q6k_raw", "mmq_q6k_wexp"]
-    calls = [
-        lambda: qig.quantize_q8_pad40(x4d, out=q84),
-        lambda: qig.mmq_q4k(W4d, OD, ID, q84, NT, y=y4, ldy=OD),
-        lambda: qig.quantize_q8_pad40(x6d, out=q86),
-        lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, y=y6, ldy=OD),
-        lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, W_exp=wexp, y=y6e, ldy=OD),
-    ]
+    steps = {
+        "pad40": {
+            "quantize_x4": lambda: qig.quantize_q8_pad40(x4d, out=q84),
+            "mmq_q4k": lambda: qig.mmq_q4k(W4d, OD, ID, q84, NT, y=y4, ldy=OD),
+            "quantize_x6": lambda: qig.quantize_q8_pad40(x6d, out=q86),
+            "mmq_q6k_raw": lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, y=y6, ldy=OD),
+            "mmq_q6k_wexp": lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, W_exp=wexp, y=y6e, ldy=OD),
+        },
+        "tiled": {
+            "quantize_tiled_x4": lambda: qig.quantize_q8_tiled(x4d, out=t84),
+            "mmq_q4k_q8t": lambda: qig.mmq_q4k_q8t(W4d, OD, ID, t84, NT, y=y4, ldy=OD),
+            "quantize_tiled_x6": lambda: qig.quantize_q8_tiled(x6d, out=t86),
+            "mmq_q6k_raw_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, y=y6, ldy=OD),
+            "mmq_q6k_wexp_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, W_exp=wexp, y=y6e, ldy=OD),
+        },
+    }
+    main_form = args.activations
+    other_form = "pad40" if main_form == "tiled" else "tiled"
+    names = list(steps[main_form])
+    calls = list(steps[main_form].values())
 
     def step():
         for fn in calls:
@@ -174,6 +196,20 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # the other activation form's step, timed the same way first (after its own
+    # warmup), so that neither form is timed on a colder GPU than the other
+    other_calls = list(steps[other_form].values())
+    for _ in range(args.warmup):
+        for fn in other_calls:
+            fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for fn in other_calls:
+            fn()
+    torch.cuda.synchronize()
+    ms_other = (time.perf_counter() - t0) / args.steps * 1e3
+
     # timed region: K whole steps back to back
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -187,7 +223,7 @@ def main():
     # pair of HIP events recorded on the launch stream (an event pair around
     # every single launch would add the event's own latency to each figure)
     per = {}
-    for n, fn in zip(names, calls):
+    for n, fn in list(steps[main_form].items()) + list(steps[other_form].items()):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -197,19 +233,24 @@ def main():
         per[n] = e0.elapsed_time(e1) * 1e3 / args.steps
     # the prepared-buffer arms (not part of the step), timed the same way
     extra = {"mmq_q4k_prepared": lambda: qig.mmq_q4k_prepared(W4p, OD, ID, q84, NT, y=y4p, ldy=OD),
-             "mmq_q6k_prepared": lambda: qig.mmq_q6k_prepared(W6p, OD, ID, q86, NT, y=y6p, ldy=OD)}
+             "mmq_q6k_prepared": lambda: qig.mmq_q6k_prepared(W6p, OD, ID, q86, NT, y=y6p, ldy=OD),
+             "mmq_q4k_prepared_q8t": lambda: qig.mmq_q4k_prepared_q8t(W4p, OD, ID, t84, NT, y=y4p, ldy=OD),
+             "mmq_q6k_prepared_q8t": lambda: qig.mmq_q6k_prepared_q8t(W6p, OD, ID, t86, NT, y=y6p, ldy=OD)}
     for n, fn in extra.items():
         per[n] = time_us(fn, reps=args.steps)
 
     gemm_ops = 2.0 * NT * OD * ID
     value = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
-    gemms = ["mmq_q4k", "mmq_q6k_raw", "mmq_q6k_wexp"]
+    gemms = [n for n in names if n.startswith("mmq")]
+    all_gemms = gemms + [n for n in steps[other_form] if n.startswith("mmq")]
     dom = max(gemms, key=lambda n: per[n])
     achieved = gemm_ops / (per[dom] * 1e-6) / 1e12
     # algorithmic bytes per launch of each GEMM: weights (raw blocks; for the dense-plane arm
     # the plane plus d and the 16 scales of each block) + pad40 plane + fp32 y, once each
-    wbytes = {"mmq_q4k": OD * (ID // 256) * 144, "mmq_q6k_raw": OD * (ID // 256) * 224,
-              "mmq_q6k_wexp": OD * ID + OD * (ID // 256) * 18}
+    # (the tiled plane has the pad40 plane's size at this nt)
+    wb = {"mmq_q4k": OD * (ID // 256) * 144, "mmq_q6k_raw": OD * (ID // 256) * 224,
+          "mmq_q6k_wexp": OD * ID + OD * (ID // 256) * 18}
+    wbytes = {n: wb[n.replace("_q8t", "")] for n in all_gemms}
     abytes = nb + NT * OD * 4
     out = {
         "metric": METRIC,
@@ -225,15 +266,18 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "q4_K + q6_K GEMMs od=id=3584, nt=512 (quantize, mmq_q4k, mmq_q6k raw, "
-                        "mmq_q6k dense-plane arm)",
+            "workload": "q4_K + q6_K GEMMs od=id=3584, nt=512 (quantize, q4_K GEMM, q6_K GEMM raw, "
+                        "q6_K GEMM dense-plane arm)",
+            "activations": main_form,
             "nt": NT, "od": OD, "id": ID, "seeds": [SEED4, SEED6],
         },
         "per_kernel_us": {k: round(v, 3) for k, v in per.items()},
-        "per_gemm_tops": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12, 1) for n in gemms + list(extra)},
+        "other_activations": {"activations": other_form, "value": round(3 * gemm_ops / (ms_other * 1e-3) / 1e12, 2),
+                              "ms_per_step": round(ms_other, 4)},
+        "per_gemm_tops": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12, 1) for n in all_gemms + list(extra)},
         "per_gemm_pct_int8_peak": {n: round(100 * gemm_ops / (per[n] * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2)
-                                   for n in gemms},
-        "per_gemm_hbm_gbs": {n: round((wbytes[n] + abytes) / (per[n] * 1e-6) / 1e9, 1) for n in gemms},
+                                   for n in all_gemms},
+        "per_gemm_hbm_gbs": {n: round((wbytes[n] + abytes) / (per[n] * 1e-6) / 1e9, 1) for n in all_gemms},
         "registration_us": {k: round(v, 3) for k, v in registration_us.items()},
         "roofline": {
             "kernel": dom,
