@@ -48,6 +48,9 @@ def parse():
     # clocks and measured up to ~10% slow, depending on what ran first
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--workload", choices=["proj", "ffn", "layer"], default="proj",
+                   help="proj: the q4_K and q6_K 3584x3584 nt=512 GEMMs (the headline); ffn: the 7B-class "
+                        "FFN GEMMs at nt=512; layer: all seven GEMMs of a 7B-class layer at nt=2630")
     p.add_argument("--activations", choices=["tiled", "pad40"], default="tiled",
                    help="activation plane of the timed step (the other form is timed and reported too)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -106,6 +109,157 @@ def cpu_baseline(W4, x4, W6, x6):
     }
 
 
+# GEMM sets of the FFN and layer workloads: (GEMM name, quant type, od, id, the
+# input it reads).  GEMMs that read the same input share one quantization.
+GEMM_SETS = {
+    "ffn": {"nt": 512, "xscale": 2.0, "gemms": [
+        ("ffn_gate", "q4_K", 18944, 3584, "x_ffn"), ("ffn_up", "q4_K", 18944, 3584, "x_ffn"),
+        ("ffn_down", "q6_K", 3584, 18944, "x_down")]},
+    "layer": {"nt": 2630, "xscale": 1.0, "gemms": [
+        ("attn_q", "q4_K", 3584, 3584, "x_attn"), ("attn_k", "q4_K", 512, 3584, "x_attn"),
+        ("attn_v", "q4_K", 512, 3584, "x_attn"), ("attn_o", "q4_K", 3584, 3584, "x_o"),
+        ("ffn_gate", "q4_K", 18944, 3584, "x_ffn"), ("ffn_up", "q4_K", 18944, 3584, "x_ffn"),
+        ("ffn_down", "q6_K", 3584, 18944, "x_down")]},
+}
+CPU_SAMPLE_TOKENS = 256
+
+
+def run_gemm_set(args):
+    """The FFN or layer workload: one quantization per distinct input (tiled
+    plane, or pad40), then its GEMMs (raw blocks; the stream-K workspace is
+    passed to every GEMM and used where the tile count calls for it)."""
+    import torch
+    import quant_integer_gemm_amd as qig
+    from quant_integer_gemm_amd import inputs
+    spec = GEMM_SETS[args.workload]
+    nt = spec["nt"]
+    dev = torch.device("cuda:0")
+    tiled = args.activations == "tiled"
+    ws = qig.new_workspace(dev)
+    xs, qs, Ws, ys, host = {}, {}, {}, {}, {}
+    for i, (name, qt, od, id_, xin) in enumerate(spec["gemms"]):
+        W, x = inputs.make_gemm_inputs(inputs.Gemm(name, qt, od, id_, nt, spec["xscale"]),
+                                       inputs.SEED_BASE + 500 + i)
+        Ws[name] = torch.from_numpy(W).to(dev)
+        host[name] = W
+        if xin not in xs:
+            xs[xin] = torch.from_numpy(x).to(dev)
+            host[xin] = x
+            nbytes = qig.q8_tiled_bytes(nt, id_) if tiled else qig.q8_pad40_bytes(nt, id_)
+            qs[xin] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ys[name] = torch.empty((nt, od), dtype=torch.float32, device=dev)
+
+    def quant(xin):
+        if tiled:
+            return lambda: qig.quantize_q8_tiled(xs[xin], out=qs[xin])
+        return lambda: qig.quantize_q8_pad40(xs[xin], out=qs[xin])
+
+    def gemm(name, qt, od, id_, xin):
+        W, q8, y = Ws[name], qs[xin], ys[name]
+        if qt == "q4_K":
+            if tiled:
+                return lambda: qig.mmq_q4k_q8t(W, od, id_, q8, nt, y=y, ldy=od, ws=ws)
+            return lambda: qig.mmq_q4k_streamk(W, od, id_, q8, nt, y=y, ldy=od, ws=ws)
+        if tiled:
+            return lambda: qig.mmq_q6k_q8t(W, 224, od, id_, q8, nt, y=y, ldy=od, ws=ws)
+        return lambda: qig.mmq_q6k_streamk(W, 224, od, id_, q8, nt, y=y, ldy=od, ws=ws)
+
+    names, calls, done = [], [], set()
+    for (name, qt, od, id_, xin) in spec["gemms"]:
+        if xin not in done:
+            names.append("quantize_" + xin)
+            calls.append(quant(xin))
+            done.add(xin)
+        names.append(name)
+        calls.append(gemm(name, qt, od, id_, xin))
+
+    def step():
+        for fn in calls:
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+
+    per = {}
+    for n, fn in zip(names, calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per[n] = e0.elapsed_time(e1) * 1e3 / args.steps
+    ops = {name: 2.0 * nt * od * id_ for (name, qt, od, id_, xin) in spec["gemms"]}
+    total_ops = sum(ops.values())
+    gemms = [g[0] for g in spec["gemms"]]
+    dom = max(gemms, key=lambda n: per[n])
+    achieved = ops[dom] / (per[dom] * 1e-6) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(total_ops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": ("7B-class FFN GEMMs at nt=512: q4_K gate/up 18944x3584, q6_K down 3584x18944"
+                         if args.workload == "ffn" else
+                         "7B-class layer at nt=2630: q4_K q, k, v, o, gate, up and q6_K down, one "
+                         "quantization per distinct input"),
+            "activations": args.activations, "nt": nt,
+            "gemms": {g[0]: f"{g[1]} {g[2]}x{g[3]}" for g in spec["gemms"]},
+        },
+        "per_kernel_us": {k: round(v, 3) for k, v in per.items()},
+        "summed_us": round(sum(per.values()), 2),
+        "per_gemm_tops": {n: round(ops[n] / (per[n] * 1e-6) / 1e12, 1) for n in gemms},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        k = min(nt, CPU_SAMPLE_TOKENS)
+        xk = {xin: np.ascontiguousarray(host[xin][:k]) for xin in {g[4] for g in spec["gemms"]}}
+        reps, total = 0, 0.0
+        while total < 10.0 and reps < 100:
+            t0 = time.perf_counter()
+            qh = {}
+            for (name, qt, od, id_, xin) in spec["gemms"]:
+                if xin not in qh:
+                    qh[xin] = oracle.quantize_q8_pad40(xk[xin])
+                if qt == "q4_K":
+                    oracle.mmq_q4k(host[name], od, id_, qh[xin], k)
+                else:
+                    oracle.mmq_q6k(host[name], 224, od, id_, qh[xin], k)
+            total += time.perf_counter() - t0
+            reps += 1
+        out["cpu_baseline"] = {
+            "value": round(total_ops * k / nt * reps / total / 1e12, 4), "unit": "TOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the first {k} of the {nt} tokens through every quantization and GEMM, "
+                      f"repeated {reps}x in {total:.1f} s",
+        }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,6 +273,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     qig.load()
+    if args.workload != "proj":
+        run_gemm_set(args)
+        return
     dev = torch.device("cuda:0")
     g4 = inputs.WORKLOADS[1][0]
     g6 = inputs.WORKLOADS[2][0]
