@@ -822,38 +822,44 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
                 load_raw<QT, ARM, ACT>(rw, src, sb + 1, tid);
             }
 
-            // Operand rings, three deep: chunk c+2's MFMA operands and scales
-            // are fetched from LDS while chunk c's epilogue runs.
-            Ab<QT> ab[3];
-            Sc<QT> sc[3];
-            f32x16 xr[2];      // activation scales, loaded one chunk ahead
+            // Operand rings: chunk c+DA's MFMA operands and weight scales and
+            // chunk c+DX's activation scales are fetched from LDS while chunk
+            // c's epilogue runs.  q4_K has the registers for one chunk more of
+            // lead (measured 1-2% faster); q6_K does not.
+            constexpr int DA = QT == 4 ? 3 : 2;
+            constexpr int DX = QT == 4 ? 2 : 1;
+            Ab<QT> ab[DA + 1];
+            Sc<QT> sc[DA + 1];
+            f32x16 xr[DX + 1];
             ChunkD<QT> dd[2];
-            load_ab(ab[0], s, 0, L);
-            load_sc(sc[0], s, 0, L);
-            xr[0] = load_x(s, 0, L);
+#pragma unroll
+            for (int k = 0; k < DA; ++k) {
+                load_ab(ab[k], s, k, L);
+                load_sc(sc[k], s, k, L);
+            }
+#pragma unroll
+            for (int k = 0; k < DX; ++k) xr[k] = load_x(s, k, L);
             MinOp mA, mB;
             if constexpr (QT == 4 && MODE == 0) {
                 mA = s.ma[L.ta][L.hh];
                 mB = s.mb[L.jb][L.hh];
             }
-            load_ab(ab[1], s, 1, L);
-            load_sc(sc[1], s, 1, L);
             dd[0] = mfma_chunk(ab[0], bias);
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
-                if (c + 2 < NCH) {
-                    load_ab(ab[(c + 2) % 3], s, c + 2, L);
-                    load_sc(sc[(c + 2) % 3], s, c + 2, L);
+                if (c + DA < NCH) {
+                    load_ab(ab[(c + DA) % (DA + 1)], s, c + DA, L);
+                    load_sc(sc[(c + DA) % (DA + 1)], s, c + DA, L);
                 }
-                if (c + 1 < NCH) xr[(c + 1) & 1] = load_x(s, c + 1, L);
+                if (c + DX < NCH) xr[(c + DX) % (DX + 1)] = load_x(s, c + DX, L);
                 ChunkD<QT> &cd = dd[c & 1];
                 if (c + 1 < NCH) {
                     ChunkD<QT> &nd = dd[(c + 1) & 1];
-                    nd = mfma_chunk(ab[(c + 1) % 3], bias);
+                    nd = mfma_chunk(ab[(c + 1) % (DA + 1)], bias);
                     pin_after(cd.v[0], nd.v[QT == 4 ? 0 : 1]);   // issue MFMA c+1 first
                     if constexpr (QT == 6) pin(cd.v[1]);
                 }
-                epilogue<QT, MODE>(cd, sc[c % 3], xr[c & 1], acc, g, tw0, jw0 + L.jb, sb, c, L);
+                epilogue<QT, MODE>(cd, sc[c % (DA + 1)], xr[c % (DX + 1)], acc, g, tw0, jw0 + L.jb, sb, c, L);
                 if constexpr (QT == 4 && MODE == 0) {
                     // the super-block's min term: hi*hi, hi*lo, lo*hi
                     if (c == 2) accm = mfma_bf16(mA.w[0], mA.w[1], mB.w[0], mB.w[1], accm);
