@@ -40,6 +40,7 @@
 //    numbered in groups of 8 row tiles and workers XCD by XCD, so the tiles
 //    running on one XCD at a time share operands in its L2.
 #include <algorithm>
+#include <atomic>
 #include <cstddef>
 #include <utility>
 
@@ -904,20 +905,21 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 // host-side launchers (argument checking is done by the C ABI layer)
 // ---------------------------------------------------------------------------
 
-// Workgroups that run at once: two per CU.
+// Workgroups that run at once: two per CU.  The CU count of each device is
+// queried once; host threads may race to fill the cache, with equal values.
 static int64_t worker_slots()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MMQ_MAX_WORKERS;
     if (dev < 0 || dev >= 64) return MMQ_MAX_WORKERS;
-    if (cached[dev] == 0) {
-        int cus = 0;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             return MMQ_MAX_WORKERS;
-        cached[dev] = cus;
+        cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return std::min<int64_t>(2 * (int64_t)cached[dev], MMQ_MAX_WORKERS);
+    return std::min<int64_t>(2 * (int64_t)cus, MMQ_MAX_WORKERS);
 }
 
 template <int QT, int ARM, int MODE, int ACT = ACT_PAD40>
