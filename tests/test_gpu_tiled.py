@@ -159,3 +159,15 @@ def test_tiled_gemm_streamk_matches_pad40_bitwise(qig, arm, nt, od, id_):
                               ws=ws)
     assert np.array_equal(y_til.view(np.uint32), y_pad.view(np.uint32))
     assert int(torch.count_nonzero(ws[-16384:]).item()) == 0
+
+
+@pytest.mark.parametrize("nt,od,id_", [(2630, 3584, 18944), (512, 18944, 3584)])
+def test_tiled_gemm_large_matches_pad40_bitwise(qig, nt, od, id_):
+    """The layer's largest GEMMs (74 super-blocks per row; 296 row tiles) on
+    both planes: bit-identical y."""
+    qt = "q6_K" if id_ == 18944 else "q4_K"
+    gm = inputs.Gemm("t", qt, od, id_, nt)
+    W, x = inputs.make_gemm_inputs(gm, inputs.SEED_BASE + 1300 + nt)
+    xd = dev(x)
+    y_pad, y_til = _gemm_pair(qig, qt, W, od, id_, qig.quantize_q8_pad40(xd), qig.quantize_q8_tiled(xd), nt)
+    assert np.array_equal(y_til.view(np.uint32), y_pad.view(np.uint32))
