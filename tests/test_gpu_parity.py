@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+import xkinds
 from quant_integer_gemm_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -36,18 +37,7 @@ def host(t):
 
 
 def _x_variant(g, nt, id_, kind):
-    x = g.standard_normal((nt, id_), dtype=np.float32)
-    if kind == "scaled2":
-        x *= np.float32(2.0)
-    elif kind == "tiny":                    # fp16-subnormal scales
-        x *= np.float32(1e-6)
-    elif kind == "ties":                    # integer inputs: many exact halves
-        x = np.round(x * 40).astype(np.float32)
-    elif kind == "zeros":                   # whole zero chunks
-        x[::3, : min(id_, 64)] = 0.0
-    elif kind == "heavy":
-        x = (g.standard_t(2.0, size=(nt, id_)) * 3).astype(np.float32)
-    return x
+    return xkinds.x_variant(g, nt, id_, kind)
 
 
 # ---------------------------------------------------------------------------
@@ -56,7 +46,7 @@ def _x_variant(g, nt, id_, kind):
 @pytest.mark.parametrize("nt,id_,kind", [
     (16, 512, "normal"), (1, 32, "normal"), (3, 96, "ties"), (37, 4096, "tiny"),
     (70, 1024, "zeros"), (9, 2048, "heavy"), (512, 3584, "normal"), (512, 18944, "scaled2"),
-    (2630, 18944, "normal"),
+    (2630, 18944, "normal"), (64, 1024, "halves"), (130, 2048, "neartie"),
 ])
 def test_quantize_bit_exact(qig, nt, id_, kind):
     g = inputs.rng(1000 + nt + id_)

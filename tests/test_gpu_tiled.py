@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+import xkinds
 from quant_integer_gemm_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -79,16 +80,11 @@ def _tiled_expected(q8, nt, id_):
 
 
 @pytest.mark.parametrize("nt,id_,kind", [(16, 512, "normal"), (70, 768, "zeros"), (1, 256, "normal"),
-                                         (129, 2304, "tiny"), (512, 3584, "normal"), (300, 18944, "heavy")])
+                                         (129, 2304, "tiny"), (512, 3584, "normal"), (300, 18944, "heavy"),
+                                         (64, 1024, "halves"), (130, 2048, "neartie")])
 def test_tiled_plane_bit_exact(qig, nt, id_, kind):
     g = inputs.rng(4000 + nt + id_)
-    x = g.standard_normal((nt, id_), dtype=np.float32)
-    if kind == "zeros":
-        x[::3, :96] = 0.0
-    elif kind == "tiny":
-        x *= np.float32(1e-6)
-    elif kind == "heavy":
-        x = (g.standard_t(2.0, size=(nt, id_)) * 3).astype(np.float32)
+    x = xkinds.x_variant(g, nt, id_, kind)
     want = _tiled_expected(oracle.quantize_q8_pad40(x), nt, id_)
     got = host(qig.quantize_q8_tiled(dev(x)))
     assert got.size == qig.q8_tiled_bytes(nt, id_) == want.size

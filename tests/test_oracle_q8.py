@@ -129,6 +129,32 @@ def test_quantize_matches_ieee_recomputation(oracle_mod):
         assert np.array_equal(qs.reshape(nt, nb32, 32), r.astype(np.int8))
 
 
+def test_quantize_exact_and_near_ties(oracle_mod):
+    # Exact halves: x / d32 = k + 1/2 exactly, so round-half-away gives k + 1
+    # for k >= 0 and k for k < 0 (closed form).  Near ties: the numpy IEEE
+    # re-derivation decides each one from the correctly rounded quotient.
+    import xkinds
+    g = np.random.Generator(np.random.PCG64(77))
+    nt, id_ = 6, 512
+    nb32 = id_ // 32
+    x = xkinds.x_variant(g, nt, id_, "halves")
+    _, qs, _, _ = oracle_mod.q8_fields(oracle_mod.quantize_q8_pad40(x), nt, id_)
+    xc = x.reshape(nt, nb32, 32).astype(np.float64)
+    d = np.max(np.abs(xc), axis=2, keepdims=True) / 127.0     # a power of two
+    v = xc / d
+    want = np.where(np.abs(v) == 127.0, v, np.where(v >= 0, v + 0.5, v - 0.5))
+    assert np.all((np.abs(v - np.trunc(v)) == 0.5) | (np.abs(v) == 127.0))
+    assert np.array_equal(qs.reshape(nt, nb32, 32), want.astype(np.int8))
+    x = xkinds.x_variant(g, nt, id_, "neartie")
+    _, qs, _, _ = oracle_mod.q8_fields(oracle_mod.quantize_q8_pad40(x), nt, id_)
+    xc = x.reshape(nt, nb32, 32)
+    d32 = np.max(np.abs(xc), axis=2) / np.float32(127.0)
+    v = (xc / d32[..., None]).astype(np.float64)
+    r = np.where(v >= 0, np.floor(v + 0.5), np.ceil(v - 0.5))
+    assert np.count_nonzero(np.abs(np.abs(v - np.trunc(v)) - 0.5) < 1e-5) > nt * id_ // 2
+    assert np.array_equal(qs.reshape(nt, nb32, 32), r.astype(np.int8))
+
+
 def test_quantize_row_stride(oracle_mod):
     g = np.random.Generator(np.random.PCG64(3))
     x = g.standard_normal((5, 160), dtype=np.float32)
