@@ -465,16 +465,18 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r, i
             const int c = 4 * h + qq;
             if constexpr (ARM == ARM_RAW) {
                 u32x4 o[2];
-                // quarter qq: nibble z of ql, bits 2qq..2qq+1 of qh moved to 4..5
-                const int lsh = 4 - 2 * pp;    // z = 0: qh << (4 - 2pp); z = 1: qh >> 2pp
+                // quarter qq: nibble z of ql; the 2-bit field f of qh at bits
+                // 2qq..2qq+1 selects the centred high bits 16 f - 32 (mod 256)
+                // of each byte from a byte table {E0, F0, 00, 10}.
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {   // output dword 4h2+e of the chunk
                         const uint32_t ql = r.q[h2][e], qh = r.q[2 + h2][e];
-                        const uint32_t nib = z == 0 ? (ql & 0x0F0F0F0Fu) : ((ql >> 4) & 0x0F0F0F0Fu);
-                        const uint32_t hi2 = (z == 0 ? (qh << lsh) : (qh >> (2 * pp))) & 0x30303030u;
-                        o[h2][e] = q6_centre(nib + hi2);
+                        const uint32_t sel = (qh >> (2 * qq)) & 0x03030303u;
+                        const uint32_t hi = __builtin_amdgcn_perm(0u, 0x1000F0E0u, sel);
+                        const uint32_t nib = z == 0 ? ql : (ql >> 4);
+                        o[h2][e] = (nib & 0x0F0F0F0Fu) | hi;
                     }
                 st16(&s.b[c][row][16 * (0 ^ sw)], o[0]);
                 st16(&s.b[c][row][16 * (1 ^ sw)], o[1]);

@@ -152,6 +152,66 @@ def test_q4k_subnormal_scales(qig):
     _assert_close(y, oracle.mmq_q4k(W, od, id_, q8, nt), "subnormal")
 
 
+def _extreme_inputs(qtype, g, nt, od, id_):
+    """Quants at their extremes, activations +-127 (so d_a = 1 and qs = x) and
+    extreme sub-block scales: the first half of the tokens is all +127 and
+    reaches the largest |P| the formats allow."""
+    x = np.where(g.random((nt, id_)) < 0.5, -127.0, 127.0).astype(np.float32)
+    x[: nt // 2] = 127.0
+    if qtype == "q6_K":
+        W = inputs.q6k_weights(g, od, id_).reshape(od, -1, 224)
+        W[: od // 2, :, 0:192] = 0x00                    # every quant -32
+        W[od // 2:, :, 0:192] = 0xFF                     # every quant +31
+        W[:, :, 192:208] = np.where(np.arange(16) % 2 == 0, -128, 127).astype(np.int8).view(np.uint8)
+        W[:, :, 208:210] = np.array([0.5], dtype=np.float16).view(np.uint8)
+    else:
+        W = inputs.q4k_weights(g, od, id_).reshape(od, -1, 144)
+        W[:, :, 16:144] = 0xFF                           # every quant 15
+        W[:, :, 4:16] = 0xFF                             # sc = m = 63 in all 8 sub-blocks
+        W[:, :, 0:2] = np.array([0.5], dtype=np.float16).view(np.uint8)
+        W[:, :, 2:4] = np.array([0.25], dtype=np.float16).view(np.uint8)
+    return W.reshape(od, -1), x
+
+
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+def test_extreme_magnitudes(qig, qtype):
+    """|P| at its bound (16*127*32 = 65024 for q6_K, 32*127*15 = 60960 for
+    q4_K): partials bit-exact, and y of every arm within tolerance."""
+    g = inputs.rng(61)
+    nt, od, id_ = 70, 130, 512
+    W, x = _extreme_inputs(qtype, g, nt, od, id_)
+    q8 = oracle.quantize_q8_pad40(x)
+    Wd, q8d = dev(W), dev(q8)
+    if qtype == "q4_K":
+        want_p = oracle.q4k_partials(W, od, id_, q8, nt, 0, nt, 0, od)
+        got_p = host(qig.mmq_q4k_partials(Wd, od, id_, q8d, nt, 0, nt, 0, od))
+        bound = 32 * 127 * 15
+    else:
+        want_p = oracle.q6k_partials(W, 224, od, id_, q8, nt, 0, nt, 0, od)
+        got_p = host(qig.mmq_q6k_partials(Wd, 224, od, id_, q8d, nt, 0, nt, 0, od))
+        bound = 16 * 127 * 32
+    assert int(np.max(np.abs(want_p))) == bound
+    assert np.array_equal(got_p, want_p), f"{np.sum(got_p != want_p)} partials differ"
+    y_ref = _oracle_gemm(qtype, W, od, id_, q8, nt)
+    q8td = qig.quantize_q8_tiled(dev(x))
+    if qtype == "q4_K":
+        Wp = qig.prepare_q4k(Wd, od, id_)
+        ys = {"raw": qig.mmq_q4k(Wd, od, id_, q8d, nt),
+              "prepared": qig.mmq_q4k_prepared(Wp, od, id_, q8d, nt),
+              "tiled": qig.mmq_q4k_q8t(Wd, od, id_, q8td, nt),
+              "prepared tiled": qig.mmq_q4k_prepared_q8t(Wp, od, id_, q8td, nt)}
+    else:
+        We = qig.expand_q6k_dense(Wd, 224, od, id_)
+        Wp = qig.prepare_q6k(Wd, 224, od, id_)
+        ys = {"raw": qig.mmq_q6k(Wd, 224, od, id_, q8d, nt),
+              "W_exp": qig.mmq_q6k(Wd, 224, od, id_, q8d, nt, W_exp=We),
+              "prepared": qig.mmq_q6k_prepared(Wp, od, id_, q8d, nt),
+              "tiled": qig.mmq_q6k_q8t(Wd, 224, od, id_, q8td, nt),
+              "W_exp tiled": qig.mmq_q6k_q8t(Wd, 224, od, id_, q8td, nt, W_exp=We)}
+    for k, y in ys.items():
+        _assert_close(host(y), y_ref, f"{qtype} extreme {k}")
+
+
 # ---------------------------------------------------------------------------
 # partials
 # ---------------------------------------------------------------------------
