@@ -387,7 +387,10 @@ __device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t 
             r.q[2] = ld16(blk + 128 + 32 * h);            // qh bytes of this half
             r.q[3] = ld16(blk + 128 + 32 * h + 16);
         }
-        r.h = ld16(blk + 192);
+        // the 8 scale bytes of this half (sub-blocks 8h .. 8h+7)
+        const uint2 sv = *reinterpret_cast<const uint2 *>(blk + 192 + 8 * h);
+        r.h[0] = sv.x;
+        r.h[1] = sv.y;
         r.d = *reinterpret_cast<const uint32_t *>(blk + 208);
     }
 }
@@ -481,7 +484,7 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r, i
                 st16(&s.b[c][row][16 * (0 ^ sw)], o[0]);
                 st16(&s.b[c][row][16 * (1 ^ sw)], o[1]);
             }
-            const uint32_t v = r.h[c >> 1];             // scale bytes 2c, 2c+1
+            const uint32_t v = r.h[z];                  // scale bytes 2c, 2c+1 (c / 2 = 2h + z)
             const int sh = 16 * (c & 1);
             const float d = h2f(r.d);
             s.bs[c][row][0] = d * (float)(int8_t)((v >> sh) & 0xff);
@@ -671,10 +674,21 @@ __device__ __forceinline__ void store_tile(const MmqArgs &g, const f32x16 &v, in
                                            const Lane &L)
 {
     if (j < g.j1) {
+        // register i holds row tb + 8 (i / 4) + i % 4: walk a pointer down
+        // the rows; all 16 exist unless the tile reaches past t1
+        const int64_t tb = tw0 + 32 * L.wt + 4 * L.hh;
+        const int64_t ld = g.ldy;
+        float *p = g.y + tb * ld + j;
+        const int64_t rem = g.t1 - tb;
+        const int n = (int)(rem < 0 ? 0 : (rem > 32 ? 32 : rem));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t t = tw0 + 32 * L.wt + mfma_row(i, L.hh);
-            if (t < g.t1) g.y[t * g.ldy + j] = v[i];
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (8 * k + e < n) *p = v[4 * k + e];
+                p += ld;
+            }
+            p += 4 * ld;
         }
     }
 }
