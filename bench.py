@@ -85,19 +85,30 @@ def recorded_traffic(kernel: str):
 
 def cpu_baseline(W4, x4, W6, x6):
     """The oracle as it stands, on the host cores: the full step's arithmetic
-    (both quantizations and the three GEMMs), repeated until ~10 s."""
+    (both quantizations and the three GEMMs), repeated until ~10 s; also the
+    mean time of each part."""
     import oracle
     ops = 3 * 2.0 * NT * OD * ID
     reps, total = 0, 0.0
+    parts = {"quantize_x4": 0.0, "mmq_q4k": 0.0, "quantize_x6": 0.0, "mmq_q6k_raw": 0.0,
+             "expand_q6k_dense": 0.0, "mmq_q6k_wexp": 0.0}
     while total < 12.0 and reps < 200:
-        t0 = time.perf_counter()
+        t = [time.perf_counter()]
         q84 = oracle.quantize_q8_pad40(x4)
+        t.append(time.perf_counter())
         oracle.mmq_q4k(W4, OD, ID, q84, NT)
+        t.append(time.perf_counter())
         q86 = oracle.quantize_q8_pad40(x6)
+        t.append(time.perf_counter())
         oracle.mmq_q6k(W6, 224, OD, ID, q86, NT)
+        t.append(time.perf_counter())
         plane = oracle.expand_q6k_dense(W6, 224, OD, ID)
+        t.append(time.perf_counter())
         oracle.mmq_q6k_from_plane(plane, ID, 256, W6, 224, OD, ID, q86, NT)
-        total += time.perf_counter() - t0
+        t.append(time.perf_counter())
+        for k, name in enumerate(parts):
+            parts[name] += t[k + 1] - t[k]
+        total += t[-1] - t[0]
         reps += 1
     return {
         "value": round(ops * reps / total / 1e12, 4),
@@ -106,6 +117,7 @@ def cpu_baseline(W4, x4, W6, x6):
         "kind": "oracle",
         "sample": f"the full step (2 quantizations, q4_K + q6_K raw + q6_K dense-plane GEMMs, "
                   f"nt={NT}, od=id={ID}) repeated {reps}x in {total:.1f} s",
+        "parts_ms": {k: round(v / reps * 1e3, 1) for k, v in parts.items()},
     }
 
 
