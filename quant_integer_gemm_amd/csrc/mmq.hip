@@ -18,10 +18,12 @@
 //    per-(token, chunk) activation scale a per-register value, read from an
 //    fp32 table in LDS laid out in register order.
 //  * K advances one super-block (256) per step.  Step k+1's activation quants
-//    are copied global->LDS directly while step k computes; its weights (and
-//    the activation d / ssum values) are loaded to registers and decoded
-//    (nibbles / 6-bit recombination to int8, scales to fp32) into the other
-//    half of the LDS stage: one barrier per step.
+//    (and the q4_K packed nibbles, and the dense planes' quants) are copied
+//    global->LDS directly while step k computes; the rest of its weights
+//    (q6_K raw quants, recombined to centred int8; the scales, to fp32) goes
+//    through registers into the other half of the LDS stage: one barrier per
+//    step.  q4_K nibbles are split after the LDS read, one read per pair of
+//    chunks (low nibbles, then high).
 //  * Within a step a wave runs its 8 chunks as a software pipeline: the MFMA
 //    of chunk c+1 is issued before the VALU epilogue of chunk c, chunk c+2's
 //    MFMA operands and chunk c+1's scales are fetched from LDS while it runs,
@@ -54,13 +56,13 @@ constexpr int TT = 64;    // tokens per workgroup tile
 constexpr int TJ = 64;    // weight rows per workgroup tile
 constexpr int NCH = 8;    // 32-element chunks per super-block
 
-// Weight sources ("arms").  RAW: raw blocks, decoded on the way into LDS.
-// WEXP (q6_K): quants from the dense plane W_exp, copied straight into LDS;
-// d and the scales from the raw blocks.  PREP: a prepared buffer made once at
+// Weight sources ("arms").  RAW: raw blocks (q4_K: packed nibbles copied
+// into LDS, scales decoded; q6_K: decoded on the way into LDS).  WEXP (q6_K):
+// quants from the dense plane W_exp, copied straight into LDS; d and the
+// scales from the raw blocks.  PREP: a prepared buffer made once at
 // registration, with the scales as an fp32 plane loaded as they are; its
-// quants are copied straight into LDS (q6_K, one centred byte per element)
-// or split from packed nibbles as in RAW (q4_K, whose nibble plane moves
-// half the bytes of a byte plane).
+// quants are copied straight into LDS (q6_K, one centred byte per element;
+// q4_K, the nibble plane, split after the LDS read as in RAW).
 constexpr int ARM_RAW = 0, ARM_WEXP = 1, ARM_PREP = 2;
 
 // Activation sources.  PAD40: the pad40 plane; quants are copied into LDS,
@@ -93,13 +95,16 @@ struct Stage<4> {
     __attribute__((aligned(16))) uint8_t a[NCH][TT][32];   // activation quants (halves swizzled)
     float ax[NCH][TT];          // activation d as fp32, token rows in register order (x_slot)
     MinOp ma[TT][2];            // -ssum of token t, chunks 4h .. 4h+3
-    uint8_t b[NCH][TJ][32];     // weight nibbles 0..15 as int8
+    // packed nibble bytes of row j as in the block (byte 32g + i holds
+    // element 64g + i low and 64g + 32 + i high), its 16-byte unit u at
+    // position u ^ ((j / 2) % 8)
+    __attribute__((aligned(16))) uint8_t bq[TJ][128];
     float bs[NCH][TJ];          // d * sc
     MinOp mb[TJ][2];            // dmin * m of row j, chunks 4h .. 4h+3
 };
 
 static_assert(offsetof(Stage<4>, ax) == 16384 && offsetof(Stage<4>, ma) == 18432 &&
-                  offsetof(Stage<4>, b) == Q8T_RECORD,
+                  offsetof(Stage<4>, bq) == Q8T_RECORD,
               "the tiled activation record is the byte image of the first Q8T_RECORD bytes of Stage<4>");
 
 // q6_K: row TT of every chunk plane of a is all zero.  Each 16-element
@@ -155,11 +160,11 @@ __device__ __forceinline__ void pin_after(T &x, const U &y) { asm volatile("" : 
 
 
 // ---------------------------------------------------------------------------
-// Staging.  Activations are copied straight into LDS (make_src, load_act).
-// Weights go through registers and are decoded on the way into LDS: row =
-// 16 * wave + lane % 16 and part = (lane / 16) % 4, a quarter of the
-// super-block's quants:
-//   q4_K: nibble group `part` -> chunks 2part (low nibbles), 2part+1 (high);
+// Staging.  Activations and q4_K's packed nibbles are copied straight into
+// LDS (make_src, load_act, load_bq).  The scales, and q6_K's raw quants, go
+// through registers and are decoded on the way into LDS: row = 16 * wave +
+// lane % 16 and part = (lane / 16) % 4, a quarter of the super-block:
+//   q4_K: scale and min of sub-blocks `part` and `part` + 4;
 //   q6_K: half h = part/2 and pair pp = part%2 -> chunks 4h+pp and 4h+pp+2,
 //         which share the same ql bytes (low / high nibble) and qh bytes.
 // Each 16-lane group walks 16 consecutive rows, so the LDS writes are free of
@@ -169,10 +174,10 @@ __device__ __forceinline__ void pin_after(T &x, const U &y) { asm volatile("" : 
 // ---------------------------------------------------------------------------
 template <int QT, int ARM>
 struct Raw {
-    static constexpr int NQ = QT == 4 ? 2 : (ARM != ARM_RAW ? 1 : 4);
+    static constexpr int NQ = QT == 4 ? 1 : (ARM != ARM_RAW ? 1 : 4);
     u32x4 h;       // q4_K header (d, dmin, 12 scale bytes) | q6_K: 16 int8 scales |
                    // PREP: 16 bytes of the row's scale block
-    u32x4 q[NQ];   // q4_K: 32 nibble bytes | q6_K raw: ql 32 B, qh 32 B | q6_K dense arms: unused
+    u32x4 q[NQ];   // q6_K raw: ql 32 B, qh 32 B | other arms: unused
     uint32_t d;    // q6_K fp16 d (low half)
     uint32_t ad[2];   // two activation block dwords (fp16 d in the low half)
     uint32_t as[2];   // q4_K: ssum of the same two blocks
@@ -190,8 +195,7 @@ struct Src {
     uint32_t aq[2];      // this lane's quant-half sources, token halves 0/1 of the tile
     uint32_t ad[2];      // blocks of this lane's two activation d (and ssum) loads
     uint32_t wo;         // this lane's weight row
-    uint32_t qo;         // q4_K PREP: this lane's row of the nibble plane
-    uint32_t xq[2];      // this lane's W_exp copy sources, row halves 0/1 of the tile
+    uint32_t xq[2];      // this lane's weight copy sources: W_exp row halves 0/1 (q6_K), nibble copies 0/1 (q4_K)
     int64_t wstep;       // bytes per super-block along w
 };
 
@@ -242,8 +246,20 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
     // weight rows in place of tokens (a row's chunk is 32 plain bytes).
     // q4_K PREP: nibble plane, id/2 bytes per row, 128 per super-block
     s.x = ARM == ARM_RAW ? nullptr : g.Wexp + jw0 * (QT == 4 ? g.id / 2 : g.id);
-    s.qo = jl * (uint32_t)(g.id / 2);
-    {
+    if constexpr (QT == 4) {
+        // packed nibble copies: wave w's copy i fills rows 16w + 8i .. +7 of
+        // Stage::bq; lane l writes position l % 8 of row 16w + 8i + l / 8,
+        // which holds unit (l % 8) ^ ((row / 2) % 8) of the row's 128 bytes
+        const int l = tid & 63, w = tid >> 6;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 16 * w + 8 * i + (l >> 3);
+            const int u = (l & 7) ^ ((r >> 1) & 7);
+            const uint32_t rl = (uint32_t)(min(jw0 + r, g.od - 1) - jw0);
+            s.xq[i] = ARM == ARM_PREP ? rl * (uint32_t)(g.id / 2) + 16 * u
+                                      : rl * (uint32_t)(nsb * 144) + 16 + 16 * u;
+        }
+    } else {
         const int l = tid & 63;
 #pragma unroll
         for (int jh = 0; jh < 2; ++jh) {
@@ -354,6 +370,17 @@ __device__ __forceinline__ void load_wexp(Stage<QT> &st, const Src &s, int64_t s
     }
 }
 
+// q4_K: direct global->LDS copies of super-block sb's packed nibbles (raw
+// blocks or the prepared nibble plane) into Stage::bq, two per wave.
+template <int ARM>
+__device__ __forceinline__ void load_bq(Stage<4> &st, const Src &s, int64_t sb, int tid)
+{
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const uint8_t *base = ARM == ARM_PREP ? s.x + sb * 128 : s.w + sb * 144;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(base, s.xq[i], &st.bq[16 * w + 8 * i][0]);
+}
+
 template <int QT, int ARM, int ACT>
 __device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t sb, int tid)
 {
@@ -370,15 +397,8 @@ __device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t 
     const uint8_t *blk = s.w + sb * s.wstep + s.wo;
     if constexpr (ARM == ARM_PREP) {
         r.h = ld16(blk + 16 * part);
-        if constexpr (QT == 4) {
-            const uint8_t *q = s.x + sb * 128 + s.qo + 32 * part;   // nibble group `part`
-            r.q[0] = ld16(q);
-            r.q[1] = ld16(q + 16);
-        }
     } else if constexpr (QT == 4) {
         r.h = ld16(blk);
-        r.q[0] = ld16(blk + 16 + 32 * part);
-        r.q[1] = ld16(blk + 32 + 32 * part);
     } else {
         const int h = part >> 1, pp = part & 1;
         if constexpr (ARM == ARM_RAW) {
@@ -412,14 +432,6 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r, i
             m[c & 3] = hi;
             m[4 + (c & 3)] = lo;
         }
-    }
-    if constexpr (QT == 4) {
-        // nibble group `part` -> chunks 2part (low nibbles), 2part+1 (high)
-        const u32x4 w0 = r.q[0], w1 = r.q[1];
-        st16(&s.b[2 * part][row][16 * (0 ^ sw)], w0 & 0x0F0F0F0Fu);
-        st16(&s.b[2 * part][row][16 * (1 ^ sw)], w1 & 0x0F0F0F0Fu);
-        st16(&s.b[2 * part + 1][row][16 * (0 ^ sw)], (w0 >> 4) & 0x0F0F0F0Fu);
-        st16(&s.b[2 * part + 1][row][16 * (1 ^ sw)], (w1 >> 4) & 0x0F0F0F0Fu);
     }
     if constexpr (ARM == ARM_PREP) {
         // this lane's 16 bytes of the row's scale block
@@ -517,16 +529,22 @@ struct Lane {
     int pa0, pa1;  // q6_K: byte offsets in a chunk plane of the two sub-block operands (one is the zero row)
 };
 
+// Chunks are fetched in order; q4_K reads the packed unit of a chunk pair at
+// its even chunk into pk and takes the low nibbles, its odd chunk the high
+// nibbles of the same pk.
 template <int QT>
-__device__ __forceinline__ void load_ab(Ab<QT> &o, const Stage<QT> &s, int c, const Lane &L)
+__device__ __forceinline__ void load_ab(Ab<QT> &o, const Stage<QT> &s, int c, const Lane &L, u32x4 &pk)
 {
     if constexpr (QT == 4) {
         o.a0 = *reinterpret_cast<const i32x4 *>(&s.a[c][L.ta][16 * (L.hh ^ swz(L.ta))]);
+        if ((c & 1) == 0)
+            pk = *reinterpret_cast<const u32x4 *>(&s.bq[L.jb][16 * ((c + L.hh) ^ ((L.jb >> 1) & 7))]);
+        o.b = __builtin_bit_cast(i32x4, (c & 1) ? ((pk >> 4) & 0x0F0F0F0Fu) : (pk & 0x0F0F0F0Fu));
     } else {
         o.a0 = *reinterpret_cast<const i32x4 *>(&s.a[c][0][0] + L.pa0);   // first 16 elements
         o.a1 = *reinterpret_cast<const i32x4 *>(&s.a[c][0][0] + L.pa1);   // last 16
+        o.b = *reinterpret_cast<const i32x4 *>(&s.b[c][L.jb][16 * (L.hh ^ swz(L.jb))]);
     }
-    o.b = *reinterpret_cast<const i32x4 *>(&s.b[c][L.jb][16 * (L.hh ^ swz(L.jb))]);
 }
 
 template <int QT>
@@ -800,6 +818,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     Raw<QT, ARM> rw;
     stage_act<QT, ACT>(st[0], src, cur.k0, tid);
     if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[0], src, cur.k0, tid);
+    if constexpr (QT == 4) load_bq<ARM>(st[0], src, cur.k0, tid);
     load_raw<QT, ARM, ACT>(rw, src, cur.k0, tid);
     int ph = 0;   // stage holding the next super-block to compute
     for (;;) {
@@ -836,6 +855,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             if (more) {
                 stage_act<QT, ACT>(sn, src, sb + 1, tid);
                 if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(sn, src, sb + 1, tid);
+                if constexpr (QT == 4) load_bq<ARM>(sn, src, sb + 1, tid);
                 load_raw<QT, ARM, ACT>(rw, src, sb + 1, tid);
             }
 
@@ -846,12 +866,13 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             constexpr int DA = QT == 4 ? 3 : 2;
             constexpr int DX = QT == 4 ? 2 : 1;
             Ab<QT> ab[DA + 1];
+            u32x4 pk;
             Sc<QT> sc[DA + 1];
             f32x16 xr[DX + 1];
             ChunkD<QT> dd[2];
 #pragma unroll
             for (int k = 0; k < DA; ++k) {
-                load_ab(ab[k], s, k, L);
+                load_ab(ab[k], s, k, L, pk);
                 load_sc(sc[k], s, k, L);
             }
 #pragma unroll
@@ -865,7 +886,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 if (c + DA < NCH) {
-                    load_ab(ab[(c + DA) % (DA + 1)], s, c + DA, L);
+                    load_ab(ab[(c + DA) % (DA + 1)], s, c + DA, L, pk);
                     load_sc(sc[(c + DA) % (DA + 1)], s, c + DA, L);
                 }
                 if (c + DX < NCH) xr[(c + DX) % (DX + 1)] = load_x(s, c + DX, L);
@@ -904,6 +925,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             src = make_src<QT, ARM, ACT>(g, nt0, nj0, tid);
             stage_act<QT, ACT>(st[ph], src, nxt.k0, tid);
             if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[ph], src, nxt.k0, tid);
+            if constexpr (QT == 4) load_bq<ARM>(st[ph], src, nxt.k0, tid);
             load_raw<QT, ARM, ACT>(rw, src, nxt.k0, tid);
         }
         if constexpr (MODE == 0) {
