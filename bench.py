@@ -59,12 +59,24 @@ def parse():
     return p.parse_args()
 
 
+KERNEL_SOURCES = ("mmq.hip", "qig_device.h", "qig_launch.h")
+
+
 def kernel_source_digest() -> str:
-    """sha256 of the GEMM kernel source: HBM-traffic figures recorded from
-    counters are only reported while the kernel they were taken on is unchanged."""
+    """sha256 of the GEMM kernel's code (mmq.hip and the headers it includes,
+    comments and blank space removed): HBM-traffic figures recorded from
+    counters are only reported while the code they were taken on is unchanged."""
     import hashlib
-    with open(os.path.join(ROOT, "quant_integer_gemm_amd", "csrc", "mmq.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quant_integer_gemm_amd", "csrc", name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        src = "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
+        h.update(name.encode() + b"\0" + src.encode() + b"\0")
+    return h.hexdigest()
 
 
 def recorded_traffic(kernel: str):
@@ -77,7 +89,7 @@ def recorded_traffic(kernel: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("mmq_hip_sha256") != kernel_source_digest():
+    if rec.get("kernel_code_sha256") != kernel_source_digest():
         return None
     v = rec.get("bytes_per_launch", {}).get(kernel)
     return None if v is None else int(v)

@@ -75,10 +75,12 @@ constexpr int ACT_PAD40 = 0, ACT_TILED = 1;
 template <int QT>
 struct Stage;
 
-// Activation quants arrive by direct global->LDS copies (load_act); the
-// activation d and ssum values and the weights go through registers
-// (load_raw / store_raw): d is widened to fp32, ssum and the weights' dmin*m
-// are split into bf16 pairs for the min-term MFMA, the weights are decoded.
+// Activation quants, q4_K's packed nibbles and the dense planes' quants
+// arrive by direct global->LDS copies (load_act, load_bq, load_wexp); pad40
+// activation d and ssum values, the weight scales and q6_K's raw quants go
+// through registers (load_raw / store_raw): d is widened to fp32, ssum and
+// the weights' dmin*m are split into bf16 pairs for the min-term MFMA, the
+// scales are decoded and q6_K's quants recombined.
 
 // q4_K min term.  -sum_c ssum(t,c) * dmin*m(j,c) is a matrix product with
 // K = 8 per super-block, run on v_mfma_f32_32x32x8_bf16 with both factors
