@@ -286,7 +286,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // untracked loads only make the compiler's own counted waits stricter.  M0
 // (the LDS address register) is read when the copy issues and is restored
 // afterwards.
-__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, void *lds)
+__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32_t lds)
 {
     // base and lds are wave-uniform; readfirstlane puts them in scalar
     // registers, as the instruction requires, whatever the compiler infers.
@@ -296,7 +296,7 @@ __device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, void *
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
     const uint64_t sbase = (uint64_t)lo | ((uint64_t)hi << 32);
-    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void_t *)lds);
+    const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
     uint32_t keep;
     asm volatile("s_mov_b32 %0, m0\n\t"
                  "s_mov_b32 m0, %3\n\t"
@@ -308,79 +308,79 @@ __device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, void *
                  : "memory");
 }
 
-// Direct global->LDS copies of super-block sb's activations into stage st.
-// The data lands asynchronously; a vmcnt(0) wait plus a barrier must come
-// before any wave reads it.
+// LDS byte addresses: the copies take the stage's address (sl, computed
+// once per kernel from the __shared__ array) plus field offsets, so their
+// destinations are scalar integer arithmetic.
 template <int QT>
-__device__ __forceinline__ void load_act(Stage<QT> &st, const Src &s, int64_t sb, int tid)
+constexpr uint32_t A_PLANE = sizeof(Stage<QT>::a[0]);   // bytes per chunk plane of a
+
+// Direct global->LDS copies of super-block sb's activations into the stage at
+// LDS address sl.  The data lands asynchronously; a vmcnt(0) wait plus a
+// barrier must come before any wave reads it.
+template <int QT>
+__device__ __forceinline__ void load_act(uint32_t sl, const Src &s, int64_t sb, int tid)
 {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const uint8_t *q8 = s.q8 + sb * 320;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = 4 * w + i, c = q >> 1;
-        dma16(q8 + 40 * c, s.aq[i & 1], &st.a[c][32 * (q & 1)][0]);
+        dma16(q8 + 40 * c, s.aq[i & 1], sl + offsetof(Stage<QT>, a) + c * A_PLANE<QT> + 1024 * (q & 1));
     }
 }
 
 // Tiled activations: the record of super-block sb holds the first
 // Q8T_RECORD bytes of the q4_K stage (quants, d table, min-term operands)
 // byte for byte; q6_K takes the quants, into its chunk planes (which keep a
-// zero row after each), and the d table.  NP pieces of 1 KB, spread over the
-// four waves.
+// zero row after each), and the d table.  Pieces of 1 KB: wave w copies
+// quant pieces w, w + 4, w + 8, w + 12 (chunk p / 2, token half p % 2), then
+// piece 16 + w of the scale tables (q6_K: d only, waves 0 and 1).
 template <int QT>
-__device__ __forceinline__ void load_act_tiled(Stage<QT> &st, const Src &s, int64_t sb, int tid)
+__device__ __forceinline__ void load_act_tiled(uint32_t sl, const Src &s, int64_t sb, int tid)
 {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    constexpr int NP = QT == 4 ? 20 : 18;
     const uint8_t *rec = s.q8 + sb * Q8T_RECORD;
 #pragma unroll
-    for (int i = 0; i < (NP + 3) / 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const int p = w + 4 * i;
-        if (p < NP) {
-            uint8_t *dst;
-            if constexpr (QT == 4)
-                dst = reinterpret_cast<uint8_t *>(&st) + 1024 * p;
-            else
-                dst = p < 16 ? &st.a[p >> 1][32 * (p & 1)][0]
-                             : reinterpret_cast<uint8_t *>(&st.ax[0][0]) + 1024 * (p - 16);
-            dma16(rec + 1024 * p, s.aq[0], dst);
-        }
+        dma16(rec + 1024 * p, s.aq[0],
+              sl + offsetof(Stage<QT>, a) + (2 * i + (w >> 1)) * A_PLANE<QT> + 1024 * (w & 1));
     }
+    if (QT == 4 || w < 2) dma16(rec + 1024 * (16 + w), s.aq[0], sl + offsetof(Stage<QT>, ax) + 1024 * w);
 }
 
 template <int QT, int ACT>
-__device__ __forceinline__ void stage_act(Stage<QT> &st, const Src &s, int64_t sb, int tid)
+__device__ __forceinline__ void stage_act(uint32_t sl, const Src &s, int64_t sb, int tid)
 {
     if constexpr (ACT == ACT_TILED)
-        load_act_tiled(st, s, sb, tid);
+        load_act_tiled<QT>(sl, s, sb, tid);
     else
-        load_act(st, s, sb, tid);
+        load_act<QT>(sl, s, sb, tid);
 }
 
 // Dense arms: direct global->LDS copies of super-block sb's quants from the
 // quant plane into stage b (same completion rule as load_act).
 template <int QT>
-__device__ __forceinline__ void load_wexp(Stage<QT> &st, const Src &s, int64_t sb, int tid)
+__device__ __forceinline__ void load_wexp(uint32_t sl, const Src &s, int64_t sb, int tid)
 {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const uint8_t *x = s.x + sb * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = 4 * w + i, c = q >> 1;
-        dma16(x + 32 * c, s.xq[i & 1], &st.b[c][32 * (q & 1)][0]);
+        dma16(x + 32 * c, s.xq[i & 1], sl + offsetof(Stage<QT>, b) + c * (TJ * 32) + 1024 * (q & 1));
     }
 }
 
 // q4_K: direct global->LDS copies of super-block sb's packed nibbles (raw
 // blocks or the prepared nibble plane) into Stage::bq, two per wave.
 template <int ARM>
-__device__ __forceinline__ void load_bq(Stage<4> &st, const Src &s, int64_t sb, int tid)
+__device__ __forceinline__ void load_bq(uint32_t sl, const Src &s, int64_t sb, int tid)
 {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const uint8_t *base = ARM == ARM_PREP ? s.x + sb * 128 : s.w + sb * 144;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(base, s.xq[i], &st.bq[16 * w + 8 * i][0]);
+    for (int i = 0; i < 2; ++i) dma16(base, s.xq[i], sl + offsetof(Stage<4>, bq) + (16 * w + 8 * i) * 128);
 }
 
 template <int QT, int ARM, int ACT>
@@ -789,6 +789,7 @@ template <int QT, int ARM, int MODE, int ACT>
 __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 {
     __shared__ Stage<QT> st[2];
+    const uint32_t sl0 = (uint32_t)(uintptr_t)(lds_void_t *)&st[0];   // LDS address of stage 0
 
     // XCD-aware worker numbering: consecutive blocks go round-robin to the 8
     // XCDs, so hand each XCD a contiguous run of worker numbers (and so of
@@ -818,9 +819,9 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     tile_origin(g, cur.tile, tw0, jw0);
     Src src = make_src<QT, ARM, ACT>(g, tw0, jw0, tid);
     Raw<QT, ARM> rw;
-    stage_act<QT, ACT>(st[0], src, cur.k0, tid);
-    if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[0], src, cur.k0, tid);
-    if constexpr (QT == 4) load_bq<ARM>(st[0], src, cur.k0, tid);
+    stage_act<QT, ACT>(sl0, src, cur.k0, tid);
+    if constexpr (ARM != ARM_RAW && QT == 6) load_wexp<QT>(sl0, src, cur.k0, tid);
+    if constexpr (QT == 4) load_bq<ARM>(sl0, src, cur.k0, tid);
     load_raw<QT, ARM, ACT>(rw, src, cur.k0, tid);
     int ph = 0;   // stage holding the next super-block to compute
     for (;;) {
@@ -855,9 +856,10 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             Stage<QT> &sn = st[ph ^ 1];
             const bool more = sb + 1 < cur.k1;
             if (more) {
-                stage_act<QT, ACT>(sn, src, sb + 1, tid);
-                if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(sn, src, sb + 1, tid);
-                if constexpr (QT == 4) load_bq<ARM>(sn, src, sb + 1, tid);
+                const uint32_t sln = sl0 + (ph ^ 1) * (uint32_t)sizeof(Stage<QT>);
+                stage_act<QT, ACT>(sln, src, sb + 1, tid);
+                if constexpr (ARM != ARM_RAW && QT == 6) load_wexp<QT>(sln, src, sb + 1, tid);
+                if constexpr (QT == 4) load_bq<ARM>(sln, src, sb + 1, tid);
                 load_raw<QT, ARM, ACT>(rw, src, sb + 1, tid);
             }
 
@@ -925,9 +927,10 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             int64_t nt0, nj0;
             tile_origin(g, nxt.tile, nt0, nj0);
             src = make_src<QT, ARM, ACT>(g, nt0, nj0, tid);
-            stage_act<QT, ACT>(st[ph], src, nxt.k0, tid);
-            if constexpr (ARM != ARM_RAW && QT == 6) load_wexp(st[ph], src, nxt.k0, tid);
-            if constexpr (QT == 4) load_bq<ARM>(st[ph], src, nxt.k0, tid);
+            const uint32_t slp = sl0 + ph * (uint32_t)sizeof(Stage<QT>);
+            stage_act<QT, ACT>(slp, src, nxt.k0, tid);
+            if constexpr (ARM != ARM_RAW && QT == 6) load_wexp<QT>(slp, src, nxt.k0, tid);
+            if constexpr (QT == 4) load_bq<ARM>(slp, src, nxt.k0, tid);
             load_raw<QT, ARM, ACT>(rw, src, nxt.k0, tid);
         }
         if constexpr (MODE == 0) {
