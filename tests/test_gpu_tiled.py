@@ -81,7 +81,8 @@ def _tiled_expected(q8, nt, id_):
 
 @pytest.mark.parametrize("nt,id_,kind", [(16, 512, "normal"), (70, 768, "zeros"), (1, 256, "normal"),
                                          (129, 2304, "tiny"), (512, 3584, "normal"), (300, 18944, "heavy"),
-                                         (64, 1024, "halves"), (130, 2048, "neartie")])
+                                         (64, 1024, "halves"), (130, 2048, "neartie"),
+                                         (1000, 16384, "neartie")])   # 1024 records: two tokens per lane group
 def test_tiled_plane_bit_exact(qig, nt, id_, kind):
     g = inputs.rng(4000 + nt + id_)
     x = xkinds.x_variant(g, nt, id_, kind)
