@@ -152,6 +152,31 @@ def test_q4k_subnormal_scales(qig):
     _assert_close(y, oracle.mmq_q4k(W, od, id_, q8, nt), "subnormal")
 
 
+@pytest.mark.parametrize("qtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("od", [1, 17, 256, 512, 3584])
+@pytest.mark.parametrize("nt", [1, 15, 16, 70, 128, 256, 512, 2630])
+def test_shape_sweep(qig, qtype, nt, od):
+    """Token and row counts from one element to several tiles with ragged
+    tails, where single shapes hide tail bugs: y within tolerance of the
+    oracle, and the tiled-plane GEMM bit-identical to the pad40 one."""
+    id_ = 512
+    gm = inputs.Gemm("sweep", qtype, od, id_, nt)
+    W, x = inputs.make_gemm_inputs(gm, inputs.SEED_BASE + 500 + 7 * nt + od)
+    q8 = oracle.quantize_q8_pad40(x)
+    Wd, xd = dev(W), dev(x)
+    q8d = qig.quantize_q8_pad40(xd)
+    q8td = qig.quantize_q8_tiled(xd)
+    if qtype == "q4_K":
+        y = qig.mmq_q4k(Wd, od, id_, q8d, nt)
+        yt = qig.mmq_q4k_q8t(Wd, od, id_, q8td, nt)
+    else:
+        y = qig.mmq_q6k(Wd, 224, od, id_, q8d, nt)
+        yt = qig.mmq_q6k_q8t(Wd, 224, od, id_, q8td, nt)
+    y, yt = host(y), host(yt)
+    _assert_close(y, _oracle_gemm(qtype, W, od, id_, q8, nt), f"{qtype} {nt}x{od}x{id_}")
+    assert np.array_equal(yt.view(np.uint32), y.view(np.uint32))
+
+
 def _extreme_inputs(qtype, g, nt, od, id_):
     """Quants at their extremes, activations +-127 (so d_a = 1 and qs = x) and
     extreme sub-block scales: the first half of the tokens is all +127 and
