@@ -84,6 +84,45 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _need(t, nbytes: int, name: str):
+    """The library reads and writes through raw pointers: check here that a
+    tensor holds the bytes a call will touch (contiguous, large enough)."""
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise QigError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise QigError(f"{name} holds {have} bytes, the call needs {nbytes}")
+
+
+def _need_y(y, nt: int, od: int, ldy: int):
+    """y is addressed as y[t * ldy + j] for t < nt, j < od (fp32)."""
+    import torch
+    if nt <= 0 or od <= 0:
+        return
+    if y.dtype != torch.float32:
+        raise QigError("y must be fp32")
+    if y.dim() == 2:
+        if y.stride(1) != 1 or y.stride(0) != ldy or y.shape[0] < nt or y.shape[1] < od:
+            raise QigError(f"y must cover [{nt}][{od}] with row stride {ldy} and unit column stride")
+    elif y.dim() != 1 or not y.is_contiguous() or y.numel() < (nt - 1) * ldy + od:
+        raise QigError(f"a 1-D y must be contiguous with at least {(nt - 1) * ldy + od} elements")
+
+
+def _raw_bytes(od: int, id_: int, bstride: int) -> int:
+    return od * (id_ // 256) * bstride
+
+
+def _gemm_checks(W, wbytes, q8, q8bytes, nt, od, y, ldy, W_exp=None, id_=0, ws=None):
+    _need(W, wbytes, "W")
+    _need(q8, q8bytes, "q8")
+    _need(W_exp, od * id_, "W_exp")
+    if ws is not None:
+        _need(ws, int(load().mmq_workspace_bytes()), "ws")
+    _need_y(y, nt, od, ldy)
+
+
 def _dev_ptr(t, name):
     if t is None:
         return None
@@ -107,6 +146,7 @@ def quantize_q8_pad40(x, id_: int | None = None, out=None, stream=None):
     nbytes = q8_pad40_bytes(nt, id_)
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _need(out, nbytes, "out")
     _check(load().quantize_q8_pad40(_dev_ptr(x, "x"), nt, id_, ldx, _dev_ptr(out, "q8"), _stream(stream)),
            "quantize_q8_pad40")
     return out
@@ -125,6 +165,7 @@ def _out_y(y, nt, od, ldy, device):
 def mmq_q4k(W, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, stream=None):
     """y[nt][od] = pad40 activations x q4_K weights^T (fp32, overwritten)."""
     y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _gemm_checks(W, _raw_bytes(od, id_, 144), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy)
     _check(load().mmq_q4k(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
                           _stream(stream)), "mmq_q4k")
     return y
@@ -134,6 +175,7 @@ def mmq_q6k(W, bstride: int, od: int, id_: int, q8, nt: int, W_exp=None, y=None,
             stream=None):
     """y[nt][od] = pad40 activations x q6_K weights^T; W_exp (dense plane) optional."""
     y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _gemm_checks(W, _raw_bytes(od, id_, bstride), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, W_exp, id_)
     _check(load().mmq_q6k(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_,
                           _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy, _stream(stream)), "mmq_q6k")
     return y
@@ -144,6 +186,8 @@ def expand_q6k_dense(W, bstride: int, od: int, id_: int, out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty((od, id_), dtype=torch.int8, device=W.device)
+    _need(W, _raw_bytes(od, id_, bstride), "W")
+    _need(out, od * id_, "out")
     _check(load().expand_q6k_dense(_dev_ptr(W, "W"), bstride, od, id_, _dev_ptr(out, "W_exp"),
                                    _stream(stream)), "expand_q6k_dense")
     return out
@@ -153,6 +197,8 @@ def mmq_q4k_partials(W, od, id_, q8, nt, t0, t1, j0, j1, stream=None):
     """int32 P4[t1-t0][j1-j0][8*nsb] from the q4_K kernel (test export)."""
     import torch
     P = torch.empty((t1 - t0, j1 - j0, 8 * (id_ // 256)), dtype=torch.int32, device=W.device)
+    _need(W, _raw_bytes(od, id_, 144), "W")
+    _need(q8, q8_pad40_bytes(nt, id_), "q8")
     _check(load().mmq_q4k_partials(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8, "q8"), nt, t0, t1, j0, j1,
                                    _dev_ptr(P, "P"), _stream(stream)), "mmq_q4k_partials")
     return P
@@ -162,6 +208,9 @@ def mmq_q6k_partials(W, bstride, od, id_, q8, nt, t0, t1, j0, j1, W_exp=None, st
     """int32 P6[t1-t0][j1-j0][16*nsb] from the q6_K kernel (test export)."""
     import torch
     P = torch.empty((t1 - t0, j1 - j0, 16 * (id_ // 256)), dtype=torch.int32, device=W.device)
+    _need(W, _raw_bytes(od, id_, bstride), "W")
+    _need(q8, q8_pad40_bytes(nt, id_), "q8")
+    _need(W_exp, od * id_, "W_exp")
     _check(load().mmq_q6k_partials(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_,
                                    _dev_ptr(q8, "q8"), nt, t0, t1, j0, j1, _dev_ptr(P, "P"),
                                    _stream(stream)), "mmq_q6k_partials")
@@ -179,6 +228,8 @@ def prepare_q4k(W, od: int, id_: int, out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty(prepared_bytes("q4_K", od, id_), dtype=torch.uint8, device=W.device)
+    _need(W, _raw_bytes(od, id_, 144), "W")
+    _need(out, prepared_bytes("q4_K", od, id_), "out")
     _check(load().prepare_q4k(_dev_ptr(W, "W"), od, id_, _dev_ptr(out, "Wp"), _stream(stream)), "prepare_q4k")
     return out
 
@@ -188,6 +239,8 @@ def prepare_q6k(W, bstride: int, od: int, id_: int, out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty(prepared_bytes("q6_K", od, id_), dtype=torch.uint8, device=W.device)
+    _need(W, _raw_bytes(od, id_, bstride), "W")
+    _need(out, prepared_bytes("q6_K", od, id_), "out")
     _check(load().prepare_q6k(_dev_ptr(W, "W"), bstride, od, id_, _dev_ptr(out, "Wp"), _stream(stream)),
            "prepare_q6k")
     return out
@@ -196,6 +249,7 @@ def prepare_q6k(W, bstride: int, od: int, id_: int, out=None, stream=None):
 def mmq_q4k_prepared(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, stream=None):
     """y[nt][od] from a prepared q4_K buffer (bit-identical to mmq_q4k on the raw blocks)."""
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    _gemm_checks(Wp, prepared_bytes("q4_K", od, id_), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy)
     _check(load().mmq_q4k_prepared(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
                                    _stream(stream)), "mmq_q4k_prepared")
     return y
@@ -204,6 +258,7 @@ def mmq_q4k_prepared(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None
 def mmq_q6k_prepared(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, stream=None):
     """y[nt][od] from a prepared q6_K buffer (bit-identical to mmq_q6k on the raw blocks)."""
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    _gemm_checks(Wp, prepared_bytes("q6_K", od, id_), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy)
     _check(load().mmq_q6k_prepared(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
                                    _stream(stream)), "mmq_q6k_prepared")
     return y
@@ -239,6 +294,7 @@ def mmq_q4k_streamk(W, od: int, id_: int, q8, nt: int, y=None, ldy: int | None =
     """mmq_q4k with the work split by super-block over all CUs (stream-K)."""
     y, ldy = _out_y(y, nt, od, ldy, W.device)
     ws = workspace(W.device) if ws is None else ws
+    _gemm_checks(W, _raw_bytes(od, id_, 144), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q4k_streamk(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
                                   _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_streamk")
     return y
@@ -249,6 +305,7 @@ def mmq_q6k_streamk(W, bstride: int, od: int, id_: int, q8, nt: int, W_exp=None,
     """mmq_q6k with the work split by super-block over all CUs (stream-K)."""
     y, ldy = _out_y(y, nt, od, ldy, W.device)
     ws = workspace(W.device) if ws is None else ws
+    _gemm_checks(W, _raw_bytes(od, id_, bstride), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, W_exp, id_, ws)
     _check(load().mmq_q6k_streamk(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_,
                                   _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy, _dev_ptr(ws, "ws"),
                                   _stream(stream)), "mmq_q6k_streamk")
@@ -260,6 +317,7 @@ def mmq_q4k_prepared_streamk(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: in
     """mmq_q4k_prepared, stream-K."""
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
     ws = workspace(Wp.device) if ws is None else ws
+    _gemm_checks(Wp, prepared_bytes("q4_K", od, id_), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q4k_prepared_streamk(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"),
                                            ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_prepared_streamk")
     return y
@@ -270,6 +328,7 @@ def mmq_q6k_prepared_streamk(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: in
     """mmq_q6k_prepared, stream-K."""
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
     ws = workspace(Wp.device) if ws is None else ws
+    _gemm_checks(Wp, prepared_bytes("q6_K", od, id_), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q6k_prepared_streamk(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"),
                                            ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_prepared_streamk")
     return y
@@ -291,6 +350,7 @@ def quantize_q8_tiled(x, id_: int | None = None, out=None, stream=None):
     ldx = x.stride(0) if nt > 1 else max(x.shape[1], id_)
     if out is None:
         out = torch.empty(q8_tiled_bytes(nt, id_), dtype=torch.uint8, device=x.device)
+    _need(out, q8_tiled_bytes(nt, id_), "out")
     _check(load().quantize_q8_tiled(_dev_ptr(x, "x"), nt, id_, ldx, _dev_ptr(out, "q8t"), _stream(stream)),
            "quantize_q8_tiled")
     return out
@@ -299,6 +359,7 @@ def quantize_q8_tiled(x, id_: int | None = None, out=None, stream=None):
 def mmq_q4k_q8t(W, od: int, id_: int, q8t, nt: int, y=None, ldy: int | None = None, ws=None, stream=None):
     """mmq_q4k on a tiled activation plane; ws: None (whole tiles) or a stream-K workspace."""
     y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _gemm_checks(W, _raw_bytes(od, id_, 144), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q4k_q8t(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"), ldy,
                               _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_q8t")
     return y
@@ -308,6 +369,7 @@ def mmq_q6k_q8t(W, bstride: int, od: int, id_: int, q8t, nt: int, W_exp=None, y=
                 ws=None, stream=None):
     """mmq_q6k on a tiled activation plane; ws: None (whole tiles) or a stream-K workspace."""
     y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _gemm_checks(W, _raw_bytes(od, id_, bstride), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, W_exp, id_, ws)
     _check(load().mmq_q6k_q8t(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_, _dev_ptr(q8t, "q8t"),
                               nt, _dev_ptr(y, "y"), ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_q8t")
     return y
@@ -317,6 +379,7 @@ def mmq_q4k_prepared_q8t(Wp, od: int, id_: int, q8t, nt: int, y=None, ldy: int |
                          stream=None):
     """mmq_q4k_prepared on a tiled activation plane."""
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    _gemm_checks(Wp, prepared_bytes("q4_K", od, id_), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q4k_prepared_q8t(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"),
                                        ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_prepared_q8t")
     return y
@@ -326,6 +389,7 @@ def mmq_q6k_prepared_q8t(Wp, od: int, id_: int, q8t, nt: int, y=None, ldy: int |
                          stream=None):
     """mmq_q6k_prepared on a tiled activation plane."""
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
+    _gemm_checks(Wp, prepared_bytes("q6_K", od, id_), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q6k_prepared_q8t(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"),
                                        ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_prepared_q8t")
     return y

@@ -116,6 +116,47 @@ def test_binding_refuses_host_tensors():
         qig.quantize_q8_pad40(x)
 
 
+def test_binding_checks_buffer_sizes_before_any_launch():
+    """Tensors too small for the bytes a call touches are refused in the
+    binding (before a pointer reaches the library); right-sized host tensors
+    pass these checks and are then refused as host memory."""
+    torch = pytest.importorskip("torch")
+    nt, od, id_ = 5, 3, 512
+    W4 = torch.zeros(od * 2 * 144, dtype=torch.uint8)
+    W6 = torch.zeros(od * 2 * 224, dtype=torch.uint8)
+    q8 = torch.zeros(qig.q8_pad40_bytes(nt, id_), dtype=torch.uint8)
+    q8t = torch.zeros(qig.q8_tiled_bytes(nt, id_), dtype=torch.uint8)
+
+    def refused(fn, words):
+        with pytest.raises(qig.QigError) as e:
+            fn()
+        assert all(w in str(e.value) for w in words), str(e.value)
+
+    refused(lambda: qig.mmq_q4k(W4[:-1], od, id_, q8, nt), ["W holds"])
+    refused(lambda: qig.mmq_q4k(W4, od, id_, q8[:-1], nt), ["q8 holds"])
+    refused(lambda: qig.mmq_q6k(W6, 224, od, id_, q8, nt, W_exp=torch.zeros(od * id_ - 1, dtype=torch.int8)),
+            ["W_exp holds"])
+    refused(lambda: qig.mmq_q6k(W6, 240, od, id_, q8, nt), ["W holds"])          # wider block stride
+    refused(lambda: qig.mmq_q4k_q8t(W4, od, id_, q8t[:-1], nt), ["q8 holds"])
+    refused(lambda: qig.mmq_q4k_q8t(W4, od, id_, q8t, nt, ws=torch.zeros(16, dtype=torch.uint8)), ["ws holds"])
+    refused(lambda: qig.mmq_q4k(W4, od, id_, q8, nt, y=torch.zeros(nt, od - 1)), ["y must cover"])
+    refused(lambda: qig.mmq_q4k(W4, od, id_, q8, nt, y=torch.zeros(nt, od + 4)[:, :od], ldy=od), ["y must cover"])
+    refused(lambda: qig.mmq_q4k(W4, od, id_, q8, nt, y=torch.zeros((nt - 1) * 8 + od - 1), ldy=8),
+            ["1-D y"])
+    refused(lambda: qig.mmq_q4k_prepared(torch.zeros(qig.prepared_bytes("q4_K", od, id_) - 1, dtype=torch.uint8),
+                                         od, id_, q8, nt), ["W holds"])
+    refused(lambda: qig.quantize_q8_pad40(torch.zeros(nt, id_), out=torch.zeros(8, dtype=torch.uint8)),
+            ["out holds"])
+    refused(lambda: qig.quantize_q8_tiled(torch.zeros(nt, id_), out=q8t[:-1]), ["out holds"])
+    refused(lambda: qig.expand_q6k_dense(W6, 224, od, id_, out=torch.zeros(od, id_ - 1, dtype=torch.int8)),
+            ["out holds"])
+    refused(lambda: qig.mmq_q4k(torch.zeros(od, 2 * 288, dtype=torch.uint8)[:, ::2], od, id_, q8, nt), ["contiguous"])
+    # right sizes: past the checks, refused as host memory
+    refused(lambda: qig.mmq_q4k(W4, od, id_, q8, nt), ["GPU tensor"])
+    refused(lambda: qig.mmq_q6k_q8t(W6, 224, od, id_, q8t, nt, y=torch.zeros(nt, od + 4), ldy=od + 4),
+            ["GPU tensor"])
+
+
 def test_oracle_not_imported_by_product():
     """The product package never imports the oracle."""
     pkg = os.path.join(ROOT, "quant_integer_gemm_amd")
