@@ -34,11 +34,6 @@ __device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b, i32x16 c)
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
 // 32x32x8 bf16 -> fp32; each operand is four bf16 packed in two dwords.
 __device__ __forceinline__ f32x16 mfma_bf16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x16 c)
 {
