@@ -131,6 +131,27 @@ def _dev_ptr(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _x_rows(x, id_):
+    """(nt, ldx, id) of an activation tensor the quantizers read as
+    x[t * ldx + k] for t < nt, k < id.  Only the first id columns of each row
+    are read, so id may not exceed the row's width; the row stride is the
+    tensor's own (one row: id, which the library accepts as a stride).  The
+    last float read must lie inside the tensor's storage."""
+    import torch
+    if x.dim() != 2 or x.dtype != torch.float32 or x.stride(1) != 1:
+        raise QigError("x must be a 2-D fp32 tensor with unit column stride")
+    nt, width = x.shape
+    id_ = width if id_ is None else int(id_)
+    if id_ > width:
+        raise QigError(f"id = {id_} exceeds the {width} columns of x")
+    ldx = x.stride(0) if nt > 1 else id_
+    if nt > 0 and id_ > 0:
+        last = x.storage_offset() + (nt - 1) * ldx + id_
+        if last * 4 > x.untyped_storage().nbytes():
+            raise QigError("x's storage does not hold the rows the call reads")
+    return nt, ldx, id_
+
+
 def q8_pad40_bytes(nt: int, id_: int) -> int:
     return int(load().q8_pad40_bytes(nt, id_))
 
@@ -138,11 +159,7 @@ def q8_pad40_bytes(nt: int, id_: int) -> int:
 def quantize_q8_pad40(x, id_: int | None = None, out=None, stream=None):
     """fp32 x[nt][ldx] (GPU) -> uint8 pad40 plane of q8_pad40_bytes(nt, id) bytes."""
     import torch
-    if x.dim() != 2 or x.dtype != torch.float32 or x.stride(1) != 1:
-        raise QigError("x must be a 2-D fp32 tensor with unit column stride")
-    nt, _ = x.shape
-    id_ = x.shape[1] if id_ is None else id_
-    ldx = x.stride(0) if nt > 1 else max(x.shape[1], id_)
+    nt, ldx, id_ = _x_rows(x, id_)
     nbytes = q8_pad40_bytes(nt, id_)
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
@@ -269,17 +286,23 @@ def mmq_q6k_prepared(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: int | None
 _workspaces = {}
 
 
-def workspace(device=None):
-    """The default stream-K workspace of a device: mmq_workspace_bytes() zero bytes,
-    allocated on first use and kept.  It serves calls issued in order on one stream;
-    calls that may overlap on different streams each need a workspace of their own
-    (``new_workspace``)."""
+def workspace(device=None, stream=None):
+    """The default stream-K workspace of a (device, stream) pair:
+    mmq_workspace_bytes() zero bytes, allocated on first use and kept.  Calls on
+    one stream run in order and may share it; keying it by stream keeps calls
+    that may overlap on different streams from sharing its arrival counters.
+    Every call leaves the counters at zero; a call interrupted by a device
+    fault does not, but such a fault also ends the HIP context the workspace
+    lives in."""
     import torch
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    if stream is None:
+        stream = torch.cuda.current_stream(index)
+    key = (index, int(stream.cuda_stream))
     ws = _workspaces.get(key)
     if ws is None:
-        ws = new_workspace(dev)
+        ws = new_workspace(torch.device("cuda", index))
         _workspaces[key] = ws
     return ws
 
@@ -293,7 +316,7 @@ def new_workspace(device):
 def mmq_q4k_streamk(W, od: int, id_: int, q8, nt: int, y=None, ldy: int | None = None, ws=None, stream=None):
     """mmq_q4k with the work split by super-block over all CUs (stream-K)."""
     y, ldy = _out_y(y, nt, od, ldy, W.device)
-    ws = workspace(W.device) if ws is None else ws
+    ws = workspace(W.device, stream) if ws is None else ws
     _gemm_checks(W, _raw_bytes(od, id_, 144), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q4k_streamk(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy,
                                   _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_streamk")
@@ -304,7 +327,7 @@ def mmq_q6k_streamk(W, bstride: int, od: int, id_: int, q8, nt: int, W_exp=None,
                     ws=None, stream=None):
     """mmq_q6k with the work split by super-block over all CUs (stream-K)."""
     y, ldy = _out_y(y, nt, od, ldy, W.device)
-    ws = workspace(W.device) if ws is None else ws
+    ws = workspace(W.device, stream) if ws is None else ws
     _gemm_checks(W, _raw_bytes(od, id_, bstride), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, W_exp, id_, ws)
     _check(load().mmq_q6k_streamk(_dev_ptr(W, "W"), bstride, _dev_ptr(W_exp, "W_exp"), od, id_,
                                   _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"), ldy, _dev_ptr(ws, "ws"),
@@ -316,7 +339,7 @@ def mmq_q4k_prepared_streamk(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: in
                              stream=None):
     """mmq_q4k_prepared, stream-K."""
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
-    ws = workspace(Wp.device) if ws is None else ws
+    ws = workspace(Wp.device, stream) if ws is None else ws
     _gemm_checks(Wp, prepared_bytes("q4_K", od, id_), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q4k_prepared_streamk(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"),
                                            ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_prepared_streamk")
@@ -327,7 +350,7 @@ def mmq_q6k_prepared_streamk(Wp, od: int, id_: int, q8, nt: int, y=None, ldy: in
                              stream=None):
     """mmq_q6k_prepared, stream-K."""
     y, ldy = _out_y(y, nt, od, ldy, Wp.device)
-    ws = workspace(Wp.device) if ws is None else ws
+    ws = workspace(Wp.device, stream) if ws is None else ws
     _gemm_checks(Wp, prepared_bytes("q6_K", od, id_), q8, q8_pad40_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q6k_prepared_streamk(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8, "q8"), nt, _dev_ptr(y, "y"),
                                            ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_prepared_streamk")
@@ -343,11 +366,7 @@ def q8_tiled_bytes(nt: int, id_: int) -> int:
 def quantize_q8_tiled(x, id_: int | None = None, out=None, stream=None):
     """fp32 x[nt][ldx] (GPU) -> uint8 tiled plane of q8_tiled_bytes(nt, id) bytes."""
     import torch
-    if x.dim() != 2 or x.dtype != torch.float32 or x.stride(1) != 1:
-        raise QigError("x must be a 2-D fp32 tensor with unit column stride")
-    nt, _ = x.shape
-    id_ = x.shape[1] if id_ is None else id_
-    ldx = x.stride(0) if nt > 1 else max(x.shape[1], id_)
+    nt, ldx, id_ = _x_rows(x, id_)
     if out is None:
         out = torch.empty(q8_tiled_bytes(nt, id_), dtype=torch.uint8, device=x.device)
     _need(out, q8_tiled_bytes(nt, id_), "out")

@@ -48,9 +48,8 @@ int launch_expand_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, in
     if (n == 0) return 0;
     const int64_t grid = (n + 255) / 256;
     if (grid > 0x7fffffff) return -1;
-    hipLaunchKernelGGL(expand_q6k_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       static_cast<const uint8_t *>(W), bstride, od, id, reinterpret_cast<uint8_t *>(Wexp));
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_kernel(expand_q6k_kernel, dim3((unsigned)grid), dim3(256), stream,
+                         static_cast<const uint8_t *>(W), bstride, od, id, reinterpret_cast<uint8_t *>(Wexp));
 }
 
 }  // namespace qig

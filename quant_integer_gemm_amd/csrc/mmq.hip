@@ -997,8 +997,7 @@ static int launch(MmqArgs g, hipStream_t stream)
             G = workers;
         }
     }
-    hipLaunchKernelGGL((mmq_kernel<QT, ARM, MODE, ACT>), dim3((unsigned)G), dim3(NTHR), 0, stream, g);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_kernel(mmq_kernel<QT, ARM, MODE, ACT>, dim3((unsigned)G), dim3(NTHR), stream, g);
 }
 
 int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)

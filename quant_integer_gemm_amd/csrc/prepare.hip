@@ -82,9 +82,8 @@ int launch_prepare_q4k(const void *W, int64_t od, int64_t id, int8_t *Q, float *
     if (n == 0) return 0;
     const int64_t grid = (n + 255) / 256;
     if (grid > 0x7fffffff) return -1;
-    hipLaunchKernelGGL(prepare_q4k_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       static_cast<const uint8_t *>(W), od, id, reinterpret_cast<uint8_t *>(Q), S);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_kernel(prepare_q4k_kernel, dim3((unsigned)grid), dim3(256), stream,
+                         static_cast<const uint8_t *>(W), od, id, reinterpret_cast<uint8_t *>(Q), S);
 }
 
 int launch_prepare_q6k_scales(const void *W, int64_t bstride, int64_t od, int64_t id, float *S,
@@ -94,9 +93,8 @@ int launch_prepare_q6k_scales(const void *W, int64_t bstride, int64_t od, int64_
     if (n == 0) return 0;
     const int64_t grid = (n + 255) / 256;
     if (grid > 0x7fffffff) return -1;
-    hipLaunchKernelGGL(prepare_q6k_scales_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       static_cast<const uint8_t *>(W), bstride, od, id, S);
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_kernel(prepare_q6k_scales_kernel, dim3((unsigned)grid), dim3(256), stream,
+                         static_cast<const uint8_t *>(W), bstride, od, id, S);
 }
 
 }  // namespace qig

@@ -4,7 +4,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace qig {
+
+// Enqueue kernel<<<grid, block, 0, stream>>>(args...) and return 0, or -3 if
+// the runtime refused this launch.  The status is hipLaunchKernel's own: a
+// triple-chevron launch followed by hipGetLastError() would also report, and
+// clear, an error left on the calling thread by an earlier, unrelated call.
+template <typename... Params, typename... Args>
+inline int launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream, Args... args)
+{
+    static_assert(sizeof...(Params) == sizeof...(Args), "argument count");
+    std::tuple<Params...> held(static_cast<Params>(args)...);
+    const hipError_t e = std::apply(
+        [&](auto &...a) {
+            void *ptrs[] = {static_cast<void *>(&a)...};
+            return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream);
+        },
+        held);
+    return e == hipSuccess ? 0 : -3;
+}
 
 struct MmqLaunch {
     int qtype;               // 4 (q4_K) or 6 (q6_K)

@@ -201,9 +201,8 @@ int launch_quantize(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q
     if (nblk == 0) return 0;
     const int64_t grid = (nblk + 31) / 32;
     if (grid > 0x7fffffff) return -1;
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, nblk, nb32, ldx,
-                       static_cast<uint8_t *>(q8));
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+    return launch_kernel(quantize_kernel, dim3((unsigned)grid), dim3(256), stream, x, nblk, nb32, ldx,
+                         static_cast<uint8_t *>(q8));
 }
 
 int launch_quantize_tiled(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q8t, hipStream_t stream)
@@ -216,12 +215,10 @@ int launch_quantize_tiled(const float *x, int64_t nt, int64_t id, int64_t ldx, v
     // measured 6% faster at 2630x18944 and 7% slower at 512x3584, where the
     // halved grid no longer covers the load latency.
     if (nrec >= 1024)
-        hipLaunchKernelGGL(quantize_tiled_kernel<2>, dim3((unsigned)(nrec * 8)), dim3(256), 0, stream, x, nt, nsb,
-                           ldx, static_cast<uint8_t *>(q8t));
-    else
-        hipLaunchKernelGGL(quantize_tiled_kernel<1>, dim3((unsigned)(nrec * 16)), dim3(256), 0, stream, x, nt, nsb,
-                           ldx, static_cast<uint8_t *>(q8t));
-    return hipGetLastError() == hipSuccess ? 0 : -3;
+        return launch_kernel(quantize_tiled_kernel<2>, dim3((unsigned)(nrec * 8)), dim3(256), stream, x, nt, nsb,
+                             ldx, static_cast<uint8_t *>(q8t));
+    return launch_kernel(quantize_tiled_kernel<1>, dim3((unsigned)(nrec * 16)), dim3(256), stream, x, nt, nsb, ldx,
+                         static_cast<uint8_t *>(q8t));
 }
 
 }  // namespace qig

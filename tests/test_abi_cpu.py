@@ -157,6 +157,29 @@ def test_binding_checks_buffer_sizes_before_any_launch():
             ["GPU tensor"])
 
 
+def test_binding_checks_activation_rows():
+    """The quantizers read the first id columns of each of nt rows: id may not
+    exceed the width of x (one row, or a column-sliced view alike), and the row
+    stride is the tensor's own.  Refused before any pointer reaches the
+    library; right-shaped host tensors are then refused as host memory."""
+    torch = pytest.importorskip("torch")
+
+    def refused(fn, words):
+        with pytest.raises(qig.QigError) as e:
+            fn()
+        assert all(w in str(e.value) for w in words), str(e.value)
+
+    big = torch.zeros(4, 512)
+    for quant in (qig.quantize_q8_pad40, qig.quantize_q8_tiled):
+        refused(lambda: quant(torch.zeros(1, 160), id_=256), ["exceeds", "160 columns"])     # one row
+        refused(lambda: quant(big[:, :256], id_=512), ["exceeds", "256 columns"])           # sliced view
+        refused(lambda: quant(big[1:2, :256], id_=512), ["exceeds"])                        # one sliced row
+        refused(lambda: quant(big[:, :256]), ["GPU tensor"])                                # the view itself
+        refused(lambda: quant(torch.zeros(1, 256)), ["GPU tensor"])
+        refused(lambda: quant(torch.zeros(5, 512, dtype=torch.float64)), ["fp32"])
+        refused(lambda: quant(big.t()), ["unit column stride"])
+
+
 def test_oracle_not_imported_by_product():
     """The product package never imports the oracle."""
     pkg = os.path.join(ROOT, "quant_integer_gemm_amd")

@@ -3,9 +3,10 @@
 Bars: pad40 bytes, W_exp bytes and int32 sub-block partials bit-exact; fp32 y
 within |y - y_ref| <= max(1e-4 |y_ref|, 1e-3 rms(y_ref)) per element, y_ref
 being the oracle's fp64 result.  Shapes span several tiles (64 tokens x 64
-rows per workgroup) with ragged tails, the five workloads at full size (all
-outputs for the nt=512 GEMMs, sampled outputs for the nt=2630 layer), and the
-degenerate cases (empty inputs, one token, one row).
+rows per workgroup) with ragged tails, the five workloads at full size (every
+output of every GEMM, the nt=2630 layer included, through the pad40 calls and
+through the tiled-plane calls bench.py times), and the degenerate cases
+(empty inputs, one token, one row).
 """
 import numpy as np
 import pytest
@@ -288,29 +289,31 @@ def test_wexp_content_and_consumer(qig, nt, od, id_, bstride):
 # ---------------------------------------------------------------------------
 # full-size workloads
 # ---------------------------------------------------------------------------
-def _run_workload_gemm(qig, gm, seed, sample=None):
+def _run_workload_gemm(qig, gm, seed):
+    """Every output of one workload GEMM against the oracle (the tolerance's
+    rms floor taken from the oracle's y), through the plain pad40 call and
+    through the launch configuration bench.py times: the tiled activation
+    plane with a stream-K workspace."""
     W, x = inputs.make_gemm_inputs(gm, seed)
     nt, od, id_ = gm.nt, gm.od, gm.id
-    xd = dev(x)
+    xd, Wd = dev(x), dev(W)
     q8d = qig.quantize_q8_pad40(xd)
     q8 = oracle.quantize_q8_pad40(x)
     assert np.array_equal(host(q8d), q8)
-    y = host(_gpu_gemm(qig, gm.qtype, dev(W), od, id_, q8d, nt))
-    if sample is None:
-        _assert_close(y, _oracle_gemm(gm.qtype, W, od, id_, q8, nt), gm.name)
-        return
-    g = inputs.rng(seed + 99)
-    tt = np.concatenate([g.integers(0, nt, sample), [0, nt - 1, nt - 1, 0]])
-    jj = np.concatenate([g.integers(0, od, sample), [0, od - 1, 0, od - 1]])
+    y_ref = _oracle_gemm(gm.qtype, W, od, id_, q8, nt)
+    y = host(_gpu_gemm(qig, gm.qtype, Wd, od, id_, q8d, nt))
+    assert np.isfinite(y).all(), f"{gm.name}: non-finite outputs"
+    _assert_close(y, y_ref, gm.name)
+    q8td = qig.quantize_q8_tiled(xd)
+    ws = qig.new_workspace("cuda")
     if gm.qtype == "q4_K":
-        ref = oracle.mmq_q4k_points(W, od, id_, q8, nt, tt, jj)
+        yt = qig.mmq_q4k_q8t(Wd, od, id_, q8td, nt, ws=ws)
     else:
-        ref = oracle.mmq_q6k_points(W, 224, od, id_, q8, nt, tt, jj)
-    # the rms floor comes from the full GPU output (its rms equals the reference's
-    # to far better than the tolerance, so this only sets the floor's scale)
-    rms = float(np.sqrt(np.mean(y.astype(np.float64) ** 2)))
-    ok, worst = oracle.within_tolerance(y[tt, jj], ref, rms=rms)
-    assert ok, f"{gm.name}: worst error/allowance = {worst:.3g}"
+        yt = qig.mmq_q6k_q8t(Wd, 224, od, id_, q8td, nt, ws=ws)
+    yt = host(yt)
+    assert np.isfinite(yt).all(), f"{gm.name} tiled: non-finite outputs"
+    _assert_close(yt, y_ref, gm.name + " tiled plane, stream-K workspace")
+    assert int(torch.count_nonzero(ws[-16384:]).item()) == 0
 
 
 # ---------------------------------------------------------------------------
@@ -388,9 +391,11 @@ def test_workload_full(qig, cfg):
         _run_workload_gemm(qig, gm, inputs.SEED_BASE + cfg + 10 * i)
 
 
-def test_workload_layer_sampled(qig):
-    for i, gm in enumerate(inputs.WORKLOADS[4]):
-        _run_workload_gemm(qig, gm, inputs.SEED_BASE + 4 + 10 * i, sample=512)
+@pytest.mark.parametrize("i", range(len(inputs.WORKLOADS[4])))
+def test_workload_layer_full(qig, i):
+    """The nt=2630 layer: every output of each of its seven GEMMs."""
+    gm = inputs.WORKLOADS[4][i]
+    _run_workload_gemm(qig, gm, inputs.SEED_BASE + 4 + 10 * i)
 
 
 # ---------------------------------------------------------------------------

@@ -168,3 +168,31 @@ def test_tiled_gemm_large_matches_pad40_bitwise(qig, nt, od, id_):
     xd = dev(x)
     y_pad, y_til = _gemm_pair(qig, qt, W, od, id_, qig.quantize_q8_pad40(xd), qig.quantize_q8_tiled(xd), nt)
     assert np.array_equal(y_til.view(np.uint32), y_pad.view(np.uint32))
+
+
+@pytest.mark.parametrize("arm", ["q4_K", "q6_K", "q6_K_wexp"])
+def test_bench_path_full_oracle(qig, arm):
+    """The step bench.py times, on its own inputs (its seeds, 512 x 3584 x
+    3584): quantize_q8_tiled, then mmq_q4k_q8t or mmq_q6k_q8t on raw blocks or
+    on the dense plane, whole tiles.  The tiled plane bit-exact against the
+    oracle's quantization and every output within tolerance of the oracle."""
+    import bench
+    qt = arm[:4]
+    gm = inputs.WORKLOADS[1][0] if qt == "q4_K" else inputs.WORKLOADS[2][0]
+    assert (gm.nt, gm.od, gm.id) == (bench.NT, bench.OD, bench.ID)
+    W, x = inputs.make_gemm_inputs(gm, bench.SEED4 if qt == "q4_K" else bench.SEED6)
+    q8 = oracle.quantize_q8_pad40(x)
+    q8td = qig.quantize_q8_tiled(dev(x))
+    assert np.array_equal(host(q8td), _tiled_expected(q8, gm.nt, gm.id))
+    Wd = dev(W)
+    if qt == "q4_K":
+        y = qig.mmq_q4k_q8t(Wd, gm.od, gm.id, q8td, gm.nt)
+        ref = oracle.mmq_q4k(W, gm.od, gm.id, q8, gm.nt)
+    else:
+        We = qig.expand_q6k_dense(Wd, 224, gm.od, gm.id) if arm == "q6_K_wexp" else None
+        y = qig.mmq_q6k_q8t(Wd, 224, gm.od, gm.id, q8td, gm.nt, W_exp=We)
+        ref = oracle.mmq_q6k(W, 224, gm.od, gm.id, q8, gm.nt)
+    y = host(y)
+    assert np.isfinite(y).all()
+    ok, worst = oracle.within_tolerance(y, ref)
+    assert ok, f"bench {arm}: worst error/allowance = {worst:.3g}"
