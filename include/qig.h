@@ -243,6 +243,30 @@ int mmq_q6k_prepared_q8t(const void *Wp, int64_t od, int64_t id,
                          void *ws, hipStream_t stream);
 
 /*
+ * mmq_q4k_q8t_noalloc -- mmq_q4k_q8t with a stream-K workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The call itself
+ * allocates nothing: its workspace is the library's own, a file-scope
+ * device array of 16 MiB + 8 KiB that each GPU holds from the library's
+ * load until the process ends (partial-sum slots and arrival counters for
+ * 512 workgroups, two on each of 256 CUs).  No shape needs more: the
+ * stream-K split never uses more than 512 workgroups, so no size is refused
+ * for want of scratch.  Each call first zeroes the counters it will use
+ * (with a kernel, not hipMemsetAsync); the partial slots are written before
+ * they are read.  y is bit-identical to mmq_q4k_q8t with a workspace on a
+ * GPU with 256 CUs.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or different host threads) race and give
+ * wrong y; calls in order on one stream are safe.
+ *   arguments as mmq_q4k_q8t (ws omitted)
+ * Errors: as mmq_q4k_q8t, plus QIG_ELAUNCH when the runtime cannot give the
+ *         array's device address.
+ */
+int mmq_q4k_q8t_noalloc(const void *W, int64_t od, int64_t id,
+                        const void *q8t, int64_t nt, float *y, int64_t ldy,
+                        hipStream_t stream);
+
+/*
  * Test exports: the int32 sub-block partials of the same kernels, for the
  * window of tokens [t0, t1) and rows [j0, j1), written to
  * P[(t - t0)][(j - j0)][sub] (int32, 4-byte aligned), where sub runs over all

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     mmq_q4k_prepared_q8t,
     mmq_q4k_prepared_streamk,
     mmq_q4k_q8t,
+    mmq_q4k_q8t_noalloc,
     mmq_q4k_streamk,
     mmq_q6k,
     mmq_q6k_partials,

@@ -46,6 +46,7 @@ SIGNATURES = {
     "mmq_q6k_q8t": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q4k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q6k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+    "mmq_q4k_q8t_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
 }
 
 
@@ -411,4 +412,17 @@ def mmq_q6k_prepared_q8t(Wp, od: int, id_: int, q8t, nt: int, y=None, ldy: int |
     _gemm_checks(Wp, prepared_bytes("q6_K", od, id_), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q6k_prepared_q8t(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"),
                                        ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_prepared_q8t")
+    return y
+
+
+def mmq_q4k_q8t_noalloc(W, od: int, id_: int, q8t, nt: int, y, ldy: int | None = None, stream=None):
+    """mmq_q4k_q8t with the stream-K split on the library's own scratch: the
+    call allocates nothing (y must be given).  Calls that may overlap on one
+    GPU race on that scratch."""
+    if y is None:
+        raise QigError("mmq_q4k_q8t_noalloc allocates nothing: pass y")
+    ldy = (y.stride(0) if y.dim() == 2 else od) if ldy is None else ldy
+    _gemm_checks(W, _raw_bytes(od, id_, 144), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy)
+    _check(load().mmq_q4k_q8t_noalloc(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"), ldy,
+                                      _stream(stream)), "mmq_q4k_q8t_noalloc")
     return y

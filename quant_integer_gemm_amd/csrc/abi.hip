@@ -242,6 +242,21 @@ int mmq_q6k_q8t(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od,
     return gemm_q6k(W, bstride, W_exp, od, id, q8t, nt, y, ldy, ws, true, stream);
 }
 
+int mmq_q4k_q8t_noalloc(const void *W, int64_t od, int64_t id, const void *q8t, int64_t nt, float *y, int64_t ldy,
+                        hipStream_t stream)
+{
+    int rc = check_gemm(W, od, id, q8t, nt, y, ldy, 144);
+    if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    void *ws = qig::mmq_scratch();
+    if (!ws) return QIG_ELAUNCH;
+    qig::MmqLaunch L = {4, W, nullptr, q8t, y, nullptr, 144, od, id, nt, ldy, 0, nt, 0, od};
+    L.ws = ws;
+    L.q8_tiled = true;
+    L.ws_workers = qig::MMQ_SCRATCH_WORKERS;
+    L.clear_counters = true;
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
 int mmq_q4k_prepared_q8t(const void *Wp, int64_t od, int64_t id, const void *q8t, int64_t nt, float *y, int64_t ldy,
                          void *ws, hipStream_t stream)
 {

@@ -43,6 +43,7 @@
 //    running on one XCD at a time share operands in its L2.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <cstddef>
 #include <utility>
 
@@ -950,23 +951,30 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 
 // Workgroups that run at once: two per CU.  The CU count of each device is
 // queried once; host threads may race to fill the cache, with equal values.
-static int64_t worker_slots()
+static int64_t worker_slots(int64_t cap)
 {
     static std::atomic<int> cached[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return MMQ_MAX_WORKERS;
-    if (dev < 0 || dev >= 64) return MMQ_MAX_WORKERS;
+    if (hipGetDevice(&dev) != hipSuccess) return cap;
+    if (dev < 0 || dev >= 64) return cap;
     int cus = cached[dev].load(std::memory_order_relaxed);
     if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return MMQ_MAX_WORKERS;
+            return cap;
         cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return std::min<int64_t>(2 * (int64_t)cus, MMQ_MAX_WORKERS);
+    return std::min<int64_t>(2 * (int64_t)cus, cap);
+}
+
+// Zero the n arrival counters of a workspace (a kernel rather than
+// hipMemsetAsync, so that the call can be captured in a HIP graph).
+__global__ __launch_bounds__(256) void clear_counters_kernel(uint32_t *cnt, int n)
+{
+    for (int i = threadIdx.x; i < n; i += 256) cnt[i] = 0;
 }
 
 template <int QT, int ARM, int MODE, int ACT = ACT_PAD40>
-static int launch(MmqArgs g, hipStream_t stream)
+static int launch(MmqArgs g, int64_t ws_workers, bool clear_counters, hipStream_t stream)
 {
     const int64_t nbt = (g.t1 - g.t0 + TT - 1) / TT;
     const int64_t nbj = (g.j1 - g.j0 + TJ - 1) / TJ;
@@ -989,13 +997,17 @@ static int launch(MmqArgs g, hipStream_t stream)
     g.sk_tiles = 0;
     const int64_t nsb = g.id / 256;
     if (MODE == 0 && g.ws != nullptr && nsb >= 2) {
-        const int64_t S = worker_slots();
+        const int64_t S = worker_slots(ws_workers);
         const int64_t workers = std::min<int64_t>(S, ntiles * nsb / MMQ_MIN_SPLIT_ITERS);
         if (ntiles * MMQ_SK_FILL_DEN <= S * MMQ_SK_FILL_NUM && workers > ntiles && ntiles * nsb < 0x7fffffff) {
             g.dp_tiles = 0;
             g.sk_tiles = (int)ntiles;
             G = workers;
         }
+    }
+    if (g.sk_tiles > 0 && clear_counters) {
+        const int rc = launch_kernel(clear_counters_kernel, dim3(1), dim3(256), stream, g.cnt, (int)(4 * G));
+        if (rc != 0) return rc;
     }
     return launch_kernel(mmq_kernel<QT, ARM, MODE, ACT>, dim3((unsigned)G), dim3(NTHR), stream, g);
 }
@@ -1020,26 +1032,57 @@ int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
     g.nbt = 0;
     g.nbj = 0;
     g.ws = static_cast<float *>(Lc.ws);
-    g.cnt = Lc.ws ? reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(Lc.ws) + MMQ_WS_PARTIAL_BYTES) : nullptr;
+    g.cnt = Lc.ws ? reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(Lc.ws) + mmq_ws_partial_bytes(Lc.ws_workers))
+                  : nullptr;
+    const int64_t wsw = Lc.ws_workers;
+    const bool clr = Lc.clear_counters;
     const bool part = Lc.P != nullptr;
     if (Lc.q8_tiled) {
         // whole-output GEMMs only (the partials exports read pad40)
         if (part) return -1;
         if (Lc.qtype == 4)
-            return Lc.prepared ? launch<4, ARM_PREP, 0, ACT_TILED>(g, stream) : launch<4, ARM_RAW, 0, ACT_TILED>(g, stream);
-        if (Lc.prepared) return launch<6, ARM_PREP, 0, ACT_TILED>(g, stream);
-        return Lc.Wexp ? launch<6, ARM_WEXP, 0, ACT_TILED>(g, stream) : launch<6, ARM_RAW, 0, ACT_TILED>(g, stream);
+            return Lc.prepared ? launch<4, ARM_PREP, 0, ACT_TILED>(g, wsw, clr, stream)
+                               : launch<4, ARM_RAW, 0, ACT_TILED>(g, wsw, clr, stream);
+        if (Lc.prepared) return launch<6, ARM_PREP, 0, ACT_TILED>(g, wsw, clr, stream);
+        return Lc.Wexp ? launch<6, ARM_WEXP, 0, ACT_TILED>(g, wsw, clr, stream)
+                       : launch<6, ARM_RAW, 0, ACT_TILED>(g, wsw, clr, stream);
     }
     if (Lc.qtype == 4) {
         if (Lc.prepared)
-            return part ? launch<4, ARM_PREP, 1>(g, stream) : launch<4, ARM_PREP, 0>(g, stream);
-        return part ? launch<4, ARM_RAW, 1>(g, stream) : launch<4, ARM_RAW, 0>(g, stream);
+            return part ? launch<4, ARM_PREP, 1>(g, wsw, clr, stream) : launch<4, ARM_PREP, 0>(g, wsw, clr, stream);
+        return part ? launch<4, ARM_RAW, 1>(g, wsw, clr, stream) : launch<4, ARM_RAW, 0>(g, wsw, clr, stream);
     }
     if (Lc.prepared)
-        return part ? launch<6, ARM_PREP, 1>(g, stream) : launch<6, ARM_PREP, 0>(g, stream);
+        return part ? launch<6, ARM_PREP, 1>(g, wsw, clr, stream) : launch<6, ARM_PREP, 0>(g, wsw, clr, stream);
     if (Lc.Wexp)
-        return part ? launch<6, ARM_WEXP, 1>(g, stream) : launch<6, ARM_WEXP, 0>(g, stream);
-    return part ? launch<6, ARM_RAW, 1>(g, stream) : launch<6, ARM_RAW, 0>(g, stream);
+        return part ? launch<6, ARM_WEXP, 1>(g, wsw, clr, stream) : launch<6, ARM_WEXP, 0>(g, wsw, clr, stream);
+    return part ? launch<6, ARM_RAW, 1>(g, wsw, clr, stream) : launch<6, ARM_RAW, 0>(g, wsw, clr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The library's own stream-K workspace, for callers that cannot allocate.
+// Each device holds its own copy of this array from load to process exit; the
+// host resolves its device address once per device (with that device
+// current) and passes that address to the kernels -- the array's name in host
+// code is only a host-side stand-in.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MMQ_SCRATCH_BYTES];
+
+void *mmq_scratch(void)
+{
+    static std::atomic<void *> addr[64];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    return p;
 }
 
 }  // namespace qig

@@ -36,8 +36,10 @@ struct MmqLaunch {
     int64_t bstride, od, id, nt, ldy;
     int64_t t0, t1, j0, j1;  // output window
     bool prepared = false;   // W / Wexp point into a prepared buffer
-    void *ws = nullptr;      // stream-K workspace (MMQ_WS_BYTES, zeroed once) or nullptr
+    void *ws = nullptr;      // stream-K workspace (mmq_ws_bytes(ws_workers), zeroed once) or nullptr
     bool q8_tiled = false;   // q8 is a tiled plane (launch_quantize_tiled), not pad40
+    int64_t ws_workers = 1024;     // workgroups the workspace has partial slots and counters for
+    bool clear_counters = false;   // zero the arrival counters before a split launch
 };
 
 // Stream-K workspace: two 64 x 64 fp32 partial-sum slots per worker, then
@@ -47,11 +49,21 @@ constexpr int64_t MMQ_MAX_WORKERS = 1024;
 constexpr int64_t MMQ_MIN_SPLIT_ITERS = 4;
 // stream-K only for a single round of tiles filling at most NUM/DEN of the slots
 constexpr int64_t MMQ_SK_FILL_NUM = 3, MMQ_SK_FILL_DEN = 4;
-constexpr int64_t MMQ_WS_PARTIAL_BYTES = MMQ_MAX_WORKERS * 2 * 64 * 64 * 4;
-constexpr int64_t MMQ_WS_BYTES = MMQ_WS_PARTIAL_BYTES + MMQ_MAX_WORKERS * 16;
+// Bytes of a workspace for `workers` workgroups: the partial slots, then the
+// counters.
+constexpr int64_t mmq_ws_partial_bytes(int64_t workers) { return workers * 2 * 64 * 64 * 4; }
+constexpr int64_t mmq_ws_bytes(int64_t workers) { return mmq_ws_partial_bytes(workers) + workers * 16; }
+constexpr int64_t MMQ_WS_BYTES = mmq_ws_bytes(MMQ_MAX_WORKERS);
+// The library's own workspace for calls that cannot allocate: a file-scope
+// device array sized for two workgroups on each of 256 CUs.
+constexpr int64_t MMQ_SCRATCH_WORKERS = 512;
+constexpr int64_t MMQ_SCRATCH_BYTES = mmq_ws_bytes(MMQ_SCRATCH_WORKERS);
 
 // All return 0, -1 (grid too large) or -3 (launch error).
 int launch_mmq(const MmqLaunch &L, hipStream_t stream);
+// Device address of this device's library scratch (MMQ_SCRATCH_BYTES), found
+// once per device; nullptr if the runtime cannot resolve it.
+void *mmq_scratch(void);
 int launch_quantize(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q8,
                     hipStream_t stream);
 int launch_expand_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, int8_t *Wexp,
