@@ -15,10 +15,21 @@ beforehand (it is registration-time work) and timed separately, as are the
 prepared-buffer GEMMs (registration-time quant + fp32 scale planes), which are
 reported per kernel but are not part of the step.
 
+Before the W warmup steps the step runs back to back for --spinup-s seconds
+(untimed), so that a short --warmup does not time a GPU that is still ramping
+its clock; the shader clock under the step's load is then measured with a
+one-wave cycle-count spin on a second stream.
+
 Prints one JSON line: value = int8 TOPS of the whole step (3 GEMMs x
 2*nt*od*id ops / step time), the per-kernel average durations from HIP
-events recorded on the launch stream, a roofline entry for the dominant
-kernel and the CPU oracle timed on the host cores.
+events recorded on the launch stream (K launches back to back), per-launch
+medians and minima over --launches launches each, warm and cold (a 512 MiB
+write before each launch), a roofline entry for the dominant kernel against
+the int8 MFMA peak (also at the measured clock) and against HBM, and the CPU
+oracle timed on the host cores.
+
+``--summarize-profiles DIR`` writes the profiles/ summaries from rocprofv3
+outputs instead (see summarize_profiles).
 """
 from __future__ import annotations
 
@@ -56,6 +67,14 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy 3x (outside the timed region) so that "
                         "HBM counters taken over this run can be scaled by a kernel of known traffic")
+    p.add_argument("--spinup-s", type=float, default=0.3,
+                   help="seconds of back-to-back steps before the warmup steps, so that the GPU is at its "
+                        "steady clock whatever --warmup is")
+    p.add_argument("--launches", type=int, default=100,
+                   help="launches per kernel for the per-launch medians (warm, and cold after a 512 MiB write)")
+    p.add_argument("--summarize-profiles", metavar="DIR",
+                   help="instead of benchmarking: turn the rocprofv3 outputs under DIR (trace/, fetch/, write/, "
+                        "sqA/, sqB/) into the summaries under profiles/")
     return p.parse_args()
 
 
@@ -95,6 +114,110 @@ def recorded_traffic(kernel: str):
     return None if v is None else int(v)
 
 
+def smi_clock_mhz():
+    """Graphics clock of GPU 0 in MHz as the SMI library reports it, or None."""
+    try:
+        import torch
+        mhz = torch.cuda.clock_rate(0)
+        return int(mhz) if mhz else None
+    except Exception:
+        return None
+
+
+def shader_clock_mhz(step, busy_steps):
+    """Shader clock under load: while `busy_steps` steps run on the current
+    stream, a one-wave kernel on a second stream spins for a fixed count of
+    shader-clock cycles (s_memtime); its duration between HIP events gives
+    the clock the GPU ran at meanwhile.  Median of three."""
+    import torch
+    side = torch.cuda.Stream()
+    cycles = 1 << 21
+    out = []
+    for _ in range(3):
+        for _ in range(busy_steps):
+            step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            e0.record()
+            torch.cuda._sleep(cycles)
+            e1.record()
+        torch.cuda.synchronize()
+        out.append(cycles / (e0.elapsed_time(e1) * 1e3))
+    out.sort()
+    return round(out[1])
+
+
+def spin_up(step, seconds):
+    """Run `step` back to back for `seconds` of wall time (untimed), so that
+    the timed steps do not start on a GPU still ramping its clock.  Returns
+    the number of steps run and the clocks: the shader clock measured under
+    the step's load, and the SMI's reading taken with steps queued."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    n, burst, smi = 0, 20, []
+    while time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        for _ in range(burst):
+            step()
+        n += burst
+        mhz = smi_clock_mhz()
+        if mhz:
+            smi.append(mhz)
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 < 0.02 and burst < 640:
+            burst *= 2   # keep about 20 ms of work queued per burst
+    smi.sort()
+    return n, {"shader_mhz": shader_clock_mhz(step, burst),
+               "smi_mhz": smi[len(smi) // 2] if smi else None}
+
+
+def per_launch_us(fn, n, flush=None):
+    """Median and minimum of n launches of fn, each between its own pair of
+    HIP events on the launch stream; with `flush`, a write of 512 MiB (which
+    evicts the L2s and the 256 MB Infinity Cache) runs before each launch,
+    outside its events."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for k, (e0, e1) in enumerate(evs):
+        if flush is not None:
+            flush(k)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    return {"median": round(ts[len(ts) // 2], 3), "min": round(ts[0], 3)}
+
+
+def oracle_single_thread(W4, x4, W6, x6, sample_tokens=128):
+    """The oracle on one thread: workload 0 in full, and the q4_K / q6_K
+    projection GEMMs (workloads 1 and 2) on their first `sample_tokens`
+    tokens, scaled to all 512."""
+    import oracle
+    from quant_integer_gemm_amd import inputs
+    g0 = inputs.WORKLOADS[0][0]
+    W0, x0 = inputs.make_gemm_inputs(g0, inputs.SEED_BASE)
+    oracle.set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        q80 = oracle.quantize_q8_pad40(x0)
+        oracle.mmq_q6k(W0, 224, g0.od, g0.id, q80, g0.nt)
+        c0 = time.perf_counter() - t
+        k = sample_tokens
+        t = time.perf_counter()
+        oracle.mmq_q4k(W4, OD, ID, oracle.quantize_q8_pad40(np.ascontiguousarray(x4[:k])), k)
+        c1 = (time.perf_counter() - t) * NT / k
+        t = time.perf_counter()
+        oracle.mmq_q6k(W6, 224, OD, ID, oracle.quantize_q8_pad40(np.ascontiguousarray(x6[:k])), k)
+        c2 = (time.perf_counter() - t) * NT / k
+    finally:
+        oracle.set_num_threads(0)
+    return {"threads": 1, "workload0_ms": round(c0 * 1e3, 2),
+            "q4k_3584x3584_nt512_ms": round(c1 * 1e3, 1), "q6k_3584x3584_nt512_ms": round(c2 * 1e3, 1),
+            "sample": f"workload 0 in full; the nt=512 GEMMs (quantization included) on their first {k} "
+                      f"tokens, scaled to 512"}
+
+
 def cpu_baseline(W4, x4, W6, x6):
     """The oracle as it stands, on the host cores: the full step's arithmetic
     (both quantizations and the three GEMMs), repeated until ~10 s; also the
@@ -130,6 +253,7 @@ def cpu_baseline(W4, x4, W6, x6):
         "sample": f"the full step (2 quantizations, q4_K + q6_K raw + q6_K dense-plane GEMMs, "
                   f"nt={NT}, od=id={ID}) repeated {reps}x in {total:.1f} s",
         "parts_ms": {k: round(v / reps * 1e3, 1) for k, v in parts.items()},
+        "single_thread": oracle_single_thread(W4, x4, W6, x6),
     }
 
 
@@ -201,6 +325,8 @@ def run_gemm_set(args):
         for fn in calls:
             fn()
 
+    spun, clocks = spin_up(step, args.spinup_s)
+    clock_mhz = clocks["shader_mhz"]
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -248,6 +374,8 @@ def run_gemm_set(args):
         "per_kernel_us": {k: round(v, 3) for k, v in per.items()},
         "summed_us": round(sum(per.values()), 2),
         "per_gemm_tops": {n: round(ops[n] / (per[n] * 1e-6) / 1e12, 1) for n in gemms},
+        "spinup": {"seconds": args.spinup_s, "steps": spun},
+        "clocks_mhz": clocks,
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
@@ -256,6 +384,8 @@ def run_gemm_set(args):
             "unit": "TOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": None,
+            "clock_mhz": clock_mhz,
+            "frac_at_clock": None if clock_mhz is None else round(achieved / (PEAK_INT8_TOPS * clock_mhz / 2400.0), 4),
         },
     }
     if not args.no_cpu_baseline:
@@ -284,8 +414,153 @@ def run_gemm_set(args):
     print(json.dumps(out), flush=True)
 
 
+# rocprofv3 kernel names -> the names bench.py reports
+PROFILE_NAMES = {
+    "qig::mmq_kernel<4, 0, 0, 0>": "mmq_q4k", "qig::mmq_kernel<6, 0, 0, 0>": "mmq_q6k_raw",
+    "qig::mmq_kernel<6, 1, 0, 0>": "mmq_q6k_wexp", "qig::mmq_kernel<4, 2, 0, 0>": "mmq_q4k_prepared",
+    "qig::mmq_kernel<6, 2, 0, 0>": "mmq_q6k_prepared", "qig::mmq_kernel<4, 0, 0, 1>": "mmq_q4k_q8t",
+    "qig::mmq_kernel<6, 0, 0, 1>": "mmq_q6k_raw_q8t", "qig::mmq_kernel<6, 1, 0, 1>": "mmq_q6k_wexp_q8t",
+    "qig::mmq_kernel<4, 2, 0, 1>": "mmq_q4k_prepared_q8t", "qig::mmq_kernel<6, 2, 0, 1>": "mmq_q6k_prepared_q8t",
+    "qig::prepare_q4k_kernel": "prepare_q4k", "qig::prepare_q6k_scales_kernel": "prepare_q6k (scales)",
+    "qig::quantize_kernel": "quantize_q8_pad40", "qig::quantize_tiled_kernel<1>": "quantize_q8_tiled",
+    "qig::quantize_tiled_kernel<2>": "quantize_q8_tiled (2 tokens per group)",
+    "qig::expand_q6k_kernel": "expand_q6k_dense", "__amd_rocclr_copyBuffer": "copy_256MiB (calibration)",
+}
+
+
+def _algorithmic_bytes():
+    """(read, write) bytes of one launch of each kernel at od = id = 3584,
+    nt = 512: each input and output once."""
+    nsb, q8 = ID // 256, NT * (ID // 32) * 40
+    y = NT * OD * 4
+    raw4, raw6 = OD * nsb * 144, OD * nsb * 224
+    wexp = OD * ID + OD * nsb * 18
+    prep4, prep6 = OD * ID // 2 + OD * nsb * 64, OD * ID + OD * nsb * 64
+    gemm = {"mmq_q4k": raw4, "mmq_q6k_raw": raw6, "mmq_q6k_wexp": wexp, "mmq_q4k_prepared": prep4,
+            "mmq_q6k_prepared": prep6}
+    alg = {}
+    for k, w in gemm.items():
+        alg[k] = alg[k + "_q8t"] = (w + q8, y)
+    alg["quantize_q8_pad40"] = alg["quantize_q8_tiled"] = (NT * ID * 4, q8)
+    alg["expand_q6k_dense"] = (OD * nsb * 210, OD * ID)
+    alg["copy_256MiB (calibration)"] = (256 << 20, 256 << 20)
+    return alg
+
+
+COUNTER_SETS = [
+    ("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"),
+    ("sqA", "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT "
+            "SQ_WAIT_ANY SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"),
+    ("sqB", "SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_INSTS_SALU "
+            "SQ_WAIT_INST_LDS SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE"),
+]
+PROFILE_BENCH = "python3 /root/repo/bench.py --steps 5 --warmup 2 --launches 5 --no-cpu-baseline --copy-calibration"
+
+
+def summarize_profiles(src_dir):
+    """Write profiles/mmq_3584x3584_nt512_{kernel_trace,counters}.md and
+    profiles/mmq_traffic.json from rocprofv3 outputs under src_dir:
+    trace/t_kernel_trace.csv (kernel trace of the default bench run, whose
+    bench line is trace/bench.json) and {fetch,write,sqA,sqB}/p_counter_collection.csv
+    (one counter run each, of PROFILE_BENCH)."""
+    import collections
+    import csv
+
+    def short(k):
+        return k.replace("void ", "").split("(")[0]
+
+    tag = "mmq_3584x3584_nt512"
+    out_dir = os.path.join(ROOT, "profiles")
+    # --- kernel trace
+    disp = collections.defaultdict(list)
+    for r in csv.DictReader(open(os.path.join(src_dir, "trace", "t_kernel_trace.csv"))):
+        disp[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in disp.values())
+    tl = ["# Kernel trace: bench.py default run (q4_K / q6_K MMQ at od=id=3584, nt=512)", "",
+          "Command, from /tmp (`cd /tmp && export TMPDIR=/tmp`):", "```",
+          "timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace -o t "
+          "-- python3 /root/repo/bench.py", "```", "",
+          "Per-dispatch durations of every launch in the run: the spin-up and warmup steps, the timed steps, "
+          "the back-to-back launches behind bench.py's per-kernel averages, and 100 warm and 100 cold (after a "
+          "512 MiB write) launches per step kernel. The median is the steady warm figure; `mean` includes the "
+          "cold launches and the clock ramp at the start.", "",
+          "| kernel | calls | median us | mean us | p10 us | min us | max us | share of GPU time |",
+          "|---|---|---|---|---|---|---|---|"]
+    for k, d in sorted(disp.items(), key=lambda kv: -sum(kv[1])):
+        d = sorted(d)
+        n = PROFILE_NAMES.get(k, k)
+        tl.append(f"| {n} | {len(d)} | {d[len(d) // 2]:.2f} | {sum(d) / len(d):.2f} | {d[len(d) // 10]:.2f} | "
+                  f"{d[0]:.2f} | {d[-1]:.2f} | {100 * sum(d) / total:.1f}% |")
+    bj = os.path.join(src_dir, "trace", "bench.json")
+    if os.path.exists(bj):
+        tl += ["", "The same run's bench.py line (per-kernel figures from HIP events on the launch stream):", "```",
+               open(bj).read().strip(), "```"]
+    with open(os.path.join(out_dir, f"{tag}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(tl) + "\n")
+    # --- counters
+    cnt = collections.defaultdict(dict)
+    for sub, _ in COUNTER_SETS:
+        path = os.path.join(src_dir, sub, "p_counter_collection.csv")
+        if not os.path.exists(path):
+            continue
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            agg[short(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for k, dd in agg.items():
+            for c, v in dd.items():
+                cnt[k][c] = sum(v) / len(v)
+    copy = cnt.get("__amd_rocclr_copyBuffer", {})
+    if "FETCH_SIZE" not in copy or "WRITE_SIZE" not in copy:
+        return
+    fs = copy["FETCH_SIZE"] * 1024 / (256 << 20)
+    wsc = copy["WRITE_SIZE"] * 1024 / (256 << 20)
+    alg = _algorithmic_bytes()
+    lines = ["# HBM traffic and SQ counters: q4_K / q6_K MMQ at od=id=3584, nt=512", "",
+             "Each counter set is its own run, from /tmp (`cd /tmp && export TMPDIR=/tmp`):", "```"]
+    for sub, cs in COUNTER_SETS:
+        lines.append(f"timeout -s KILL 120 rocprofv3 --pmc {cs} --output-format csv -d gpurun_out/prof/{sub} -o p "
+                     f"-- {PROFILE_BENCH}")
+    lines += ["```", "",
+              f"Calibration: a plain 256 MiB device copy reads FETCH_SIZE = {copy['FETCH_SIZE']:.0f} KiB and "
+              f"WRITE_SIZE = {copy['WRITE_SIZE']:.0f} KiB per dispatch against 262144 KiB moved each way, so HBM "
+              f"bytes = FETCH_SIZE x 1024 / {fs:.4f} + WRITE_SIZE x 1024 / {wsc:.4f}.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB (scaled) | HBM write MB | algorithmic read MB "
+              "| algorithmic write MB | read / algorithmic |",
+              "|---|---|---|---|---|---|---|---|"]
+    traffic = {}
+    for k, n in PROFILE_NAMES.items():
+        c = cnt.get(k)
+        if not c or "FETCH_SIZE" not in c or "WRITE_SIZE" not in c or n not in alg:
+            continue
+        rb, wb = c["FETCH_SIZE"] * 1024 / fs, c["WRITE_SIZE"] * 1024 / wsc
+        ar, aw = alg[n]
+        traffic[n] = int(round(rb + wb))
+        lines.append(f"| {n} | {c['FETCH_SIZE']:.1f} | {c['WRITE_SIZE']:.1f} | {rb / 1e6:.2f} | {wb / 1e6:.2f} | "
+                     f"{ar / 1e6:.2f} | {aw / 1e6:.2f} | {rb / ar:.2f} |")
+    cols = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES",
+            "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+            "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_SALU"]
+    lines += ["", "SQ counters per dispatch (means over the run's dispatches; SQ_* summed over the chip):", "",
+              "| kernel | " + " | ".join(cols) + " |", "|---" * (len(cols) + 1) + "|"]
+    for k, n in PROFILE_NAMES.items():
+        c = cnt.get(k)
+        if not c or "SQ_INSTS_VALU" not in c:
+            continue
+        lines.append(f"| {n} | " + " | ".join(f"{c[x]:.0f}" if x in c else "—" for x in cols) + " |")
+    with open(os.path.join(out_dir, f"{tag}_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    rec = {"kernel_code_sha256": kernel_source_digest(), "fetch_scale": round(fs, 5), "write_scale": round(wsc, 5),
+           "source": f"profiles/{tag}_counters.md",
+           "bytes_per_launch": {k: v for k, v in traffic.items() if k.startswith("mmq")}}
+    with open(os.path.join(out_dir, "mmq_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is described, not built).", file=sys.stderr)
@@ -366,6 +641,8 @@ def main():
         for fn in calls:
             fn()
 
+    spun, clocks = spin_up(step, args.spinup_s)
+    clock_mhz = clocks["shader_mhz"]
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -412,6 +689,17 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         per[n] = e0.elapsed_time(e1) * 1e3 / args.steps
+    # per-launch distributions of the step's kernels: warm (back to back) and
+    # cold (a 512 MiB write before each launch, outside its events), against
+    # the same event pair around a one-element kernel
+    tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    event_overhead = per_launch_us(lambda: tiny.add_(1.0), args.launches)
+    per_launch = {}
+    for n, fn in steps[main_form].items():
+        per_launch[n] = {"warm": per_launch_us(fn, args.launches),
+                         "cold": per_launch_us(fn, args.launches, flush=lambda k: flush_buf.fill_(k & 255))}
+    del flush_buf
     # the prepared-buffer arms (not part of the step), timed the same way
     extra = {"mmq_q4k_prepared": lambda: qig.mmq_q4k_prepared(W4p, OD, ID, q84, NT, y=y4p, ldy=OD),
              "mmq_q6k_prepared": lambda: qig.mmq_q6k_prepared(W6p, OD, ID, q86, NT, y=y6p, ldy=OD),
@@ -433,6 +721,8 @@ def main():
           "mmq_q6k_wexp": OD * ID + OD * (ID // 256) * 18}
     wbytes = {n: wb[n.replace("_q8t", "")] for n in all_gemms}
     abytes = nb + NT * OD * 4
+    dom_bytes = wbytes[dom] + abytes
+    clock_frac = None if clock_mhz is None else round(achieved / (PEAK_INT8_TOPS * clock_mhz / 2400.0), 4)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -460,6 +750,10 @@ def main():
                                    for n in all_gemms},
         "per_gemm_hbm_gbs": {n: round((wbytes[n] + abytes) / (per[n] * 1e-6) / 1e9, 1) for n in all_gemms},
         "registration_us": {k: round(v, 3) for k, v in registration_us.items()},
+        "per_launch_us": per_launch,
+        "event_overhead_us": event_overhead,
+        "spinup": {"seconds": args.spinup_s, "steps": spun},
+        "clocks_mhz": clocks,
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
@@ -468,6 +762,12 @@ def main():
             "unit": "TOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": recorded_traffic(dom),
+            "clock_mhz": clock_mhz,
+            "frac_at_clock": clock_frac,
+            "hbm_algorithmic_bytes": dom_bytes,
+            "hbm_achieved_gbs": round(dom_bytes / (per[dom] * 1e-6) / 1e9, 1),
+            "hbm_peak_gbs": PEAK_HBM_GBS,
+            "hbm_frac": round(dom_bytes / (per[dom] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         },
     }
     if not args.no_cpu_baseline:

@@ -86,6 +86,8 @@ def _load():
     lib.oracle_mmq_q6k_from_plane.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -234,6 +236,11 @@ def mmq_q6k_from_plane(plane, row_stride, sb_stride, W, bstride, od, id_, q8, nt
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of later oracle calls (0 restores the default)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def within_tolerance(y: np.ndarray, y_ref: np.ndarray, rms: float | None = None,

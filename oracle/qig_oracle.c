@@ -569,3 +569,16 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Harness control, not arithmetic: the thread count of later calls (n <= 0
+ * restores the OpenMP default).  Timings of the oracle on one thread use it. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    static int dflt = 0;
+    if (dflt == 0) dflt = omp_get_max_threads();
+    omp_set_num_threads(n > 0 ? n : dflt);
+#else
+    (void)n;
+#endif
+}
