@@ -243,6 +243,43 @@ int mmq_q6k_prepared_q8t(const void *Wp, int64_t od, int64_t id,
                          void *ws, hipStream_t stream);
 
 /*
+ * q6_K limb buffers -- a registration-time form of q6_K weights in which each
+ * 16-element sub-block's int8 scale is folded into the quants (the pages'
+ * pre-expansion of r43 "PC-sampling attribution" s3.2 and r44 "W_exp stride
+ * mismatch root cause" s2.1-s2.4, carried one step further: the sub-block
+ * scales of r44 s1.1 leave the GEMM's epilogue).  Per element, with c6 the
+ * centred quant (r44 s3.2) and sc its sub-block's scale,
+ *   v = sc * c6 (|v| <= 4096) = 128 * H + L,  H = floor(v / 128) in
+ *   [-32, 32], L = v - 128 * H in [0, 127],
+ * both stored as int8.  A buffer of q6k_limbs_bytes(od, id) =
+ * 2*od*id + od*(id/256)*4 bytes holds
+ *   H plane   int8 [od][id] at offset 0 (row stride id)
+ *   L plane   int8 [od][id] at offset od*id
+ *   d plane   fp32 [od][id/256] at offset 2*od*id: the super-block's fp16 d
+ * The layout is part of this contract.  It takes 2.3 times the raw blocks'
+ * memory (25.7 MB against 11.2 MB at 3584 x 3584).
+ *
+ * mmq_q6k_limbs_q8t -- y[nt][od] of the q6_K GEMM from a limb buffer and a
+ * tiled activation plane (quantize_q8_tiled).  Per 32-element chunk the
+ * exact integer Q = sum(qa * v) = 128 P_H + P_L comes from two int8 MFMAs;
+ *   y = sum_sb d * sum_c da(t, c) * Q(t, j, c),
+ * in fp32 (the same value as mmq_q6k up to rounding order: within the
+ * output tolerance, not bit-identical).
+ *   W      raw q6_K plane as for mmq_q6k (prepare only), 16-byte aligned
+ *   Wl     the limb buffer, 16-byte aligned; prepare writes every byte
+ *   q8t, nt, y, ldy, ws as for mmq_q6k_q8t
+ * q6k_limbs_bytes returns 0 for invalid shapes.  prepare_q6k_limbs:
+ * QIG_EINVAL (od < 0, id <= 0 or id % 256, bad bstride), QIG_EALIGN,
+ * QIG_ELAUNCH.  mmq_q6k_limbs_q8t: as mmq_q6k_q8t.
+ */
+size_t q6k_limbs_bytes(int64_t od, int64_t id);
+int prepare_q6k_limbs(const void *W, int64_t bstride, int64_t od, int64_t id,
+                      void *Wl, hipStream_t stream);
+int mmq_q6k_limbs_q8t(const void *Wl, int64_t od, int64_t id,
+                      const void *q8t, int64_t nt, float *y, int64_t ldy,
+                      void *ws, hipStream_t stream);
+
+/*
  * mmq_q4k_q8t_noalloc -- mmq_q4k_q8t with a stream-K workspace, for callers
  * that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc).  The call itself

@@ -47,6 +47,9 @@ SIGNATURES = {
     "mmq_q4k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q6k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q4k_q8t_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "q6k_limbs_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "prepare_q6k_limbs": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "mmq_q6k_limbs_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
 }
 
 
@@ -412,6 +415,34 @@ def mmq_q6k_prepared_q8t(Wp, od: int, id_: int, q8t, nt: int, y=None, ldy: int |
     _gemm_checks(Wp, prepared_bytes("q6_K", od, id_), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q6k_prepared_q8t(_dev_ptr(Wp, "Wp"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"),
                                        ldy, _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_prepared_q8t")
+    return y
+
+
+# --- q6_K limb buffers (sub-block scales folded into two int8 limbs) ------------
+
+def q6k_limbs_bytes(od: int, id_: int) -> int:
+    """Size of a q6_K limb buffer: H and L planes (od*id bytes each) + fp32 d plane."""
+    return int(load().q6k_limbs_bytes(od, id_))
+
+
+def prepare_q6k_limbs(W, bstride: int, od: int, id_: int, out=None, stream=None):
+    """Raw q6_K plane -> limb buffer (v = sc*c6 = 128 H + L per element, and d)."""
+    import torch
+    if out is None:
+        out = torch.empty(q6k_limbs_bytes(od, id_), dtype=torch.uint8, device=W.device)
+    _need(W, _raw_bytes(od, id_, bstride), "W")
+    _need(out, q6k_limbs_bytes(od, id_), "out")
+    _check(load().prepare_q6k_limbs(_dev_ptr(W, "W"), bstride, od, id_, _dev_ptr(out, "Wl"), _stream(stream)),
+           "prepare_q6k_limbs")
+    return out
+
+
+def mmq_q6k_limbs_q8t(Wl, od: int, id_: int, q8t, nt: int, y=None, ldy: int | None = None, ws=None, stream=None):
+    """y[nt][od] of the q6_K GEMM from a limb buffer and a tiled activation plane."""
+    y, ldy = _out_y(y, nt, od, ldy, Wl.device)
+    _gemm_checks(Wl, q6k_limbs_bytes(od, id_), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
+    _check(load().mmq_q6k_limbs_q8t(_dev_ptr(Wl, "Wl"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"), ldy,
+                                    _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_limbs_q8t")
     return y
 
 

@@ -242,6 +242,36 @@ int mmq_q6k_q8t(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od,
     return gemm_q6k(W, bstride, W_exp, od, id, q8t, nt, y, ldy, ws, true, stream);
 }
 
+size_t q6k_limbs_bytes(int64_t od, int64_t id)
+{
+    if (od < 0 || id <= 0 || id % 256 != 0) return 0;
+    return 2 * (size_t)od * (size_t)id + (size_t)od * (size_t)(id / 256) * 4u;
+}
+
+int prepare_q6k_limbs(const void *W, int64_t bstride, int64_t od, int64_t id, void *Wl, hipStream_t stream)
+{
+    if (bad_bstride(bstride) || od < 0 || id <= 0 || id % 256 != 0) return QIG_EINVAL;
+    if (od == 0) return QIG_OK;
+    if (!W || !Wl) return QIG_EINVAL;
+    if (!aligned(W, 16) || !aligned(Wl, 16)) return QIG_EALIGN;
+    return rc_from_launch(qig::launch_prepare_q6k_limbs(W, bstride, od, id, Wl, stream));
+}
+
+int mmq_q6k_limbs_q8t(const void *Wl, int64_t od, int64_t id, const void *q8t, int64_t nt, float *y, int64_t ldy,
+                      void *ws, hipStream_t stream)
+{
+    int rc = check_gemm(Wl, od, id, q8t, nt, y, ldy, 64);
+    if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    if (ws && !aligned(ws, 16)) return QIG_EALIGN;
+    const uint8_t *H = static_cast<const uint8_t *>(Wl);
+    const void *D = H + 2 * od * id;
+    qig::MmqLaunch L = {6, D, reinterpret_cast<const int8_t *>(H), q8t, y, nullptr, 64, od, id, nt, ldy, 0, nt, 0, od};
+    L.ws = ws;
+    L.q8_tiled = true;
+    L.limbs = true;
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
 int mmq_q4k_q8t_noalloc(const void *W, int64_t od, int64_t id, const void *q8t, int64_t nt, float *y, int64_t ldy,
                         hipStream_t stream)
 {

@@ -65,6 +65,9 @@ constexpr int NCH = 8;    // 32-element chunks per super-block
 // quants are copied straight into LDS (q6_K, one centred byte per element;
 // q4_K, the nibble plane, split after the LDS read as in RAW).
 constexpr int ARM_RAW = 0, ARM_WEXP = 1, ARM_PREP = 2;
+// LIMB (q6_K, tiled activations only): a limb buffer (prepare_q6k_limbs) run
+// by mmq_limbs_kernel, below.
+constexpr int ARM_LIMB = 3;
 
 // Activation sources.  PAD40: the pad40 plane; quants are copied into LDS,
 // d and ssum go through registers (d widened, -ssum split into bf16 pairs).
@@ -945,6 +948,250 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// q6_K limb arm (a registration-time limb buffer; tiled activations).
+//
+// The limb buffer folds each 16-element sub-block's int8 scale into the
+// quants: v = sc * c6 = 128 H + L with int8 limbs H in [-32, 32] and L in
+// [0, 127].  For a 32-element chunk the exact integer Q = sum qa * v =
+// 128 P_H + P_L comes from two MFMAs, and the chunk's weight scale is d alone,
+// applied once per super-block.  The MFMA is transposed here (weight rows are
+// its rows, tokens its columns), so the activation scale of a chunk is one
+// value per lane rather than sixteen per lane from LDS.  Per chunk and output:
+//   t = fma(D_H, 128, -129 M) = 128 P_H - M          (D = M + P, M = 1.5 2^23;
+//   u = fma(D_L, 1, t)         = 128 P_H + P_L = Q    both exact: |Q| < 2^24)
+//   acc = fma(u, da, acc)                            (rounded once)
+// and per super-block y = fma(acc, d, y).  Steps are half super-blocks (four
+// chunks): the limbs double the weight bytes, and a full super-block stage
+// pair would not leave room for two workgroups per CU.
+// ---------------------------------------------------------------------------
+constexpr int LCH = 4;   // chunks per step
+
+struct StageL {
+    __attribute__((aligned(16))) uint8_t a[LCH][TT][32];   // activation quants (token rows, halves swizzled)
+    float ax[LCH][TT];                                      // activation d (fp32), x_slot order
+    __attribute__((aligned(16))) uint8_t h[LCH][TJ][32];   // H limbs (weight rows, halves swizzled)
+    __attribute__((aligned(16))) uint8_t l[LCH][TJ][32];   // L limbs
+    __attribute__((aligned(16))) float dw[TJ];             // the super-block's weight d, row-slot order (odd steps)
+};
+static_assert(sizeof(StageL) >= 4 * 32 * 33 * 4, "a stage holds the four waves' transpose scratch");
+
+struct SrcL {
+    const uint8_t *q8;    // the tile's tiled activation records
+    const uint8_t *hl;    // H plane at the tile's first row (L plane: + od * id)
+    const float *d;       // d plane at the tile's first row
+    uint32_t xq[2];       // this lane's limb copy sources: rows 32 jh + l / 2, half (l & 1) ^ swz(row)
+    uint32_t dro;         // d of row tid (< 64), clamped: its offset in rows of the d plane
+};
+
+__device__ __forceinline__ SrcL make_src_l(const MmqArgs &g, int64_t tw0, int64_t jw0, int tid)
+{
+    SrcL s;
+    const int64_t nsb = g.id / 256;
+    s.q8 = g.q8 + (tw0 / 64) * nsb * Q8T_RECORD;
+    s.hl = g.Wexp + jw0 * g.id;
+    s.d = reinterpret_cast<const float *>(g.W) + jw0 * nsb;
+    const int l = tid & 63;
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh) {
+        const int r = 32 * jh + (l >> 1);
+        const uint32_t rl = (uint32_t)(min(jw0 + r, g.od - 1) - jw0);
+        s.xq[jh] = rl * (uint32_t)g.id + 16 * ((l & 1) ^ swz(r));
+    }
+    s.dro = (uint32_t)(min(jw0 + (tid & 63), g.od - 1) - jw0);
+    return s;
+}
+
+// Half P (0 or 1) of step (sb, hs)'s copies into the stage at LDS address sl.
+// Wave w brings chunk w of the half: its activation quants (two 1 KB pieces
+// of the record), and its H and L limbs (two 1 KB copies each, one per
+// 32-row half); wave 0 also the activation d of the half.
+template <int P>
+__device__ __forceinline__ void issue_l(uint32_t sl, const SrcL &s, const MmqArgs &g, int64_t sb, int hs, int tid)
+{
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lo = 16u * (uint32_t)(tid & 63);
+    const int c = 4 * hs + w;   // chunk of the super-block
+    const uint8_t *rec = s.q8 + sb * Q8T_RECORD;
+    const uint8_t *hb = s.hl + 256 * sb + 32 * c;
+    if constexpr (P == 0) {
+        dma16(rec + 2048 * c, lo, sl + offsetof(StageL, a) + 2048 * w);
+        dma16(rec + 2048 * c + 1024, lo, sl + offsetof(StageL, a) + 2048 * w + 1024);
+        dma16(hb, s.xq[0], sl + offsetof(StageL, h) + 2048 * w);
+        if (w == 0) dma16(rec + 16384 + 1024 * hs, lo, sl + offsetof(StageL, ax));
+    } else {
+        const uint8_t *lb = hb + g.od * g.id;
+        dma16(hb, s.xq[1], sl + offsetof(StageL, h) + 2048 * w + 1024);
+        dma16(lb, s.xq[0], sl + offsetof(StageL, l) + 2048 * w);
+        dma16(lb, s.xq[1], sl + offsetof(StageL, l) + 2048 * w + 1024);
+    }
+}
+
+__device__ __forceinline__ float fma3c(float a, float b, float c)
+{
+    asm("v_fma_f32 %0, %1, %2, %3" : "=v"(a) : "v"(a), "v"(b), "v"(c));
+    return a;
+}
+
+__global__ __launch_bounds__(NTHR, 2) void mmq_limbs_kernel(MmqArgs g)
+{
+    __shared__ StageL st[2];
+    const uint32_t sl0 = (uint32_t)(uintptr_t)(lds_void_t *)&st[0];
+
+    const int G = gridDim.x, b = blockIdx.x;
+    const int q = G / 8, r = G % 8, x = b % 8;
+    const int v = x * q + min(x, r) + b / 8;
+    const int nsb = (int)(g.id / 256);
+    const int I = g.sk_tiles * nsb;
+    int it = (int)((int64_t)v * I / G);
+    const int it_end = (int)((int64_t)(v + 1) * I / G);
+    int dpt = v;
+    Work cur = next_work(g, dpt, it, it_end, G, nsb);
+    if (cur.k1 == 0) return;
+
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+    const int wt = wave & 1, wr = wave >> 1;   // token group, row group (the layout finish_tile expects)
+    const int tok = 32 * wt + (lane & 31), row = 32 * wr + (lane & 31);
+    const int pa = 32 * tok + 16 * (hh ^ swz(tok));    // byte offsets within a chunk plane
+    const int pw = 32 * row + 16 * (hh ^ swz(row));
+    const int xs = x_slot(tok);
+    const float c128 = 128.0f, cm = -129.0f * MAGIC_F;
+    int64_t tw0, jw0;
+    tile_origin(g, cur.tile, tw0, jw0);
+    SrcL src = make_src_l(g, tw0, jw0, tid);
+    issue_l<0>(sl0, src, g, cur.k0, 0, tid);
+    issue_l<1>(sl0, src, g, cur.k0, 0, tid);
+    int ph = 0;
+    for (;;) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        i32x16 bias;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bias[i] = MAGIC_I;
+        f32x16 acc, y;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc[i] = 0.0f;
+            y[i] = 0.0f;
+        }
+        const int nsteps = 2 * (cur.k1 - cur.k0);
+        float dnext = 0.0f;
+        for (int stp = 0; stp < nsteps; ++stp) {
+            const int64_t sb = cur.k0 + (stp >> 1);
+            const int hs = stp & 1;
+            const StageL &s = st[ph];
+            const bool more = stp + 1 < nsteps;
+            const uint32_t sln = sl0 + (ph ^ 1) * (uint32_t)sizeof(StageL);
+            const int64_t sbn = cur.k0 + ((stp + 1) >> 1);
+            if (more) {
+                issue_l<0>(sln, src, g, sbn, hs ^ 1, tid);
+                issue_l<1>(sln, src, g, sbn, hs ^ 1, tid);
+                // the next step is the second half of a super-block: its d
+                if (hs == 0 && tid < 64) dnext = src.d[src.dro * nsb + sbn];
+            }
+            i32x4 ah[LCH], al[LCH], ab[LCH];
+            float xv[LCH];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                ah[c] = *reinterpret_cast<const i32x4 *>(&s.h[c][0][0] + pw);
+                al[c] = *reinterpret_cast<const i32x4 *>(&s.l[c][0][0] + pw);
+                ab[c] = *reinterpret_cast<const i32x4 *>(&s.a[c][0][0] + pa);
+                xv[c] = s.ax[c][xs];
+            }
+            i32x16 dh[2], dl[2];
+            dh[0] = mfma_i8(ah[0], ab[0], bias);
+            dl[0] = mfma_i8(al[0], ab[0], bias);
+#pragma unroll
+            for (int c = 0; c < LCH; ++c) {
+                if (c + 2 < LCH) {
+                    ah[c + 2] = *reinterpret_cast<const i32x4 *>(&s.h[c + 2][0][0] + pw);
+                    al[c + 2] = *reinterpret_cast<const i32x4 *>(&s.l[c + 2][0][0] + pw);
+                    ab[c + 2] = *reinterpret_cast<const i32x4 *>(&s.a[c + 2][0][0] + pa);
+                    xv[c + 2] = s.ax[c + 2][xs];
+                }
+                i32x16 &ch = dh[c & 1], &cl = dl[c & 1];
+                if (c + 1 < LCH) {
+                    i32x16 &nh = dh[(c + 1) & 1], &nl = dl[(c + 1) & 1];
+                    nh = mfma_i8(ah[c + 1], ab[c + 1], bias);
+                    nl = mfma_i8(al[c + 1], ab[c + 1], bias);
+                    pin_after(ch, nl);
+                    pin(cl);
+                }
+                f32x16 t;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) t[i] = fma3c(as_float(ch[i]), c128, cm);
+                pin(t);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float u;
+                    asm("v_fma_f32 %0, %1, 1.0, %2" : "=v"(u) : "v"(as_float(cl[i])), "v"(t[i]));
+                    t[i] = u;
+                }
+                pin(t);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = fma3(t[i], xv[c], acc[i]);
+                pin(acc);
+            }
+            if (hs == 1) {
+                // end of the super-block: y += d * acc, with this lane's 16 rows' d
+                const f32x4 *pd = reinterpret_cast<const f32x4 *>(&s.dw[32 * wr + 16 * hh]);
+                const f32x4 d0 = pd[0], d1 = pd[1], d2 = pd[2], d3 = pd[3];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    y[i] = fma3(acc[i], d0[i], y[i]);
+                    y[4 + i] = fma3(acc[4 + i], d1[i], y[4 + i]);
+                    y[8 + i] = fma3(acc[8 + i], d2[i], y[8 + i]);
+                    y[12 + i] = fma3(acc[12 + i], d3[i], y[12 + i]);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+            }
+            if (more && hs == 0 && tid < 64) {
+                const int rr = tid;
+                st[ph ^ 1].dw[32 * (rr >> 5) + row_slot(rr & 31)] = dnext;
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            ph ^= 1;
+        }
+
+        // Issue the next item's first step, then transpose this wave's 32 x 32
+        // block through the stage just computed (free after the barrier) into
+        // finish_tile's layout (lane = weight row, registers = tokens).
+        const Work nxt = next_work(g, dpt, it, it_end, G, nsb);
+        if (nxt.k1 != 0) {
+            tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            int64_t nt0, nj0;
+            tile_origin(g, nxt.tile, nt0, nj0);
+            src = make_src_l(g, nt0, nj0, tid);
+            const uint32_t slp = sl0 + ph * (uint32_t)sizeof(StageL);
+            issue_l<0>(slp, src, g, nxt.k0, 0, tid);
+            issue_l<1>(slp, src, g, nxt.k0, 0, tid);
+        }
+        float *tp = reinterpret_cast<float *>(&st[ph ^ 1]) + wave * (32 * 33);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tp[mfma_row(i, hh) * 33 + (lane & 31)] = y[i];
+        f32x16 ys;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ys[i] = tp[(lane & 31) * 33 + mfma_row(i, hh)];
+        Lane L;
+        L.wt = wt;
+        L.hh = hh;
+        L.ta = tok;
+        L.jb = row;
+        L.l16 = lane & 15;
+        L.pa0 = L.pa1 = 0;
+        finish_tile(g, ys, cur, v, G, nsb, L, wave, lane);
+        if (nxt.k1 == 0) break;
+        cur = nxt;
+        tile_origin(g, cur.tile, tw0, jw0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host-side launchers (argument checking is done by the C ABI layer)
 // ---------------------------------------------------------------------------
@@ -1009,7 +1256,10 @@ static int launch(MmqArgs g, int64_t ws_workers, bool clear_counters, hipStream_
         const int rc = launch_kernel(clear_counters_kernel, dim3(1), dim3(256), stream, g.cnt, (int)(4 * G));
         if (rc != 0) return rc;
     }
-    return launch_kernel(mmq_kernel<QT, ARM, MODE, ACT>, dim3((unsigned)G), dim3(NTHR), stream, g);
+    if constexpr (ARM == ARM_LIMB)
+        return launch_kernel(mmq_limbs_kernel, dim3((unsigned)G), dim3(NTHR), stream, g);
+    else
+        return launch_kernel(mmq_kernel<QT, ARM, MODE, ACT>, dim3((unsigned)G), dim3(NTHR), stream, g);
 }
 
 int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
@@ -1037,6 +1287,10 @@ int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
     const int64_t wsw = Lc.ws_workers;
     const bool clr = Lc.clear_counters;
     const bool part = Lc.P != nullptr;
+    if (Lc.limbs) {
+        if (part || !Lc.q8_tiled || Lc.qtype != 6) return -1;
+        return launch<6, ARM_LIMB, 0, ACT_TILED>(g, wsw, clr, stream);
+    }
     if (Lc.q8_tiled) {
         // whole-output GEMMs only (the partials exports read pad40)
         if (part) return -1;

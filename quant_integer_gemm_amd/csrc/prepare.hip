@@ -76,6 +76,52 @@ __global__ __launch_bounds__(256) void prepare_q6k_scales_kernel(const uint8_t *
     }
 }
 
+// q6_K limb planes: one thread per (row, super-block, 16-element sub-block
+// s).  Each element's centred quant c6 (the element map of the r44 page
+// "W_exp stride mismatch root cause", s3.2) is multiplied by its sub-block's
+// int8 scale, and the product v = sc * c6 (|v| <= 4096) is split exactly into
+// two int8 limbs, H = v >> 7 (floor, in [-32, 32]) and L = v & 127, so that
+// v = 128 H + L.  The fp16 d of the super-block goes to the d plane as fp32.
+__global__ __launch_bounds__(256) void prepare_q6k_limbs_kernel(const uint8_t *__restrict__ W, int64_t bstride,
+                                                                 int64_t od, int64_t id, uint8_t *__restrict__ H,
+                                                                 uint8_t *__restrict__ L, float *__restrict__ D)
+{
+    const int64_t nsb = id / 256;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= od * nsb * 16) return;
+    const int s = (int)(gid & 15);
+    const int64_t blkno = gid >> 4;                 // j * nsb + sb
+    const int64_t j = blkno / nsb, sb = blkno % nsb;
+    const uint8_t *blk = W + blkno * bstride;
+    const int sc = (int8_t)blk[192 + s];
+    uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = 16 * s + i, n = e & 127, half = e >> 7;
+        const int lo = (blk[64 * half + (n & 63)] >> (4 * (n >> 6))) & 15;
+        const int hi = (blk[128 + 32 * half + (e & 31)] >> (2 * ((n >> 5) & 3))) & 3;
+        const int v = sc * ((lo | (hi << 4)) - 32);
+        hw[i >> 2] |= ((uint32_t)(v >> 7) & 0xffu) << (8 * (i & 3));
+        lw[i >> 2] |= (uint32_t)(v & 127) << (8 * (i & 3));
+    }
+    const int64_t off = j * id + 256 * sb + 16 * s;
+    *reinterpret_cast<u32x4 *>(H + off) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    *reinterpret_cast<u32x4 *>(L + off) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    if (s == 0) D[blkno] = h2f(*reinterpret_cast<const uint32_t *>(blk + 208));
+}
+
+int launch_prepare_q6k_limbs(const void *W, int64_t bstride, int64_t od, int64_t id, void *Wl, hipStream_t stream)
+{
+    const int64_t n = od * (id / 256) * 16;
+    if (n == 0) return 0;
+    const int64_t grid = (n + 255) / 256;
+    if (grid > 0x7fffffff) return -1;
+    uint8_t *H = static_cast<uint8_t *>(Wl);
+    return launch_kernel(prepare_q6k_limbs_kernel, dim3((unsigned)grid), dim3(256), stream,
+                         static_cast<const uint8_t *>(W), bstride, od, id, H, H + od * id,
+                         reinterpret_cast<float *>(H + 2 * od * id));
+}
+
 int launch_prepare_q4k(const void *W, int64_t od, int64_t id, int8_t *Q, float *S, hipStream_t stream)
 {
     const int64_t n = od * (id / 256) * 4;

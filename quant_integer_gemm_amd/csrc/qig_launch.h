@@ -40,6 +40,7 @@ struct MmqLaunch {
     bool q8_tiled = false;   // q8 is a tiled plane (launch_quantize_tiled), not pad40
     int64_t ws_workers = 1024;     // workgroups the workspace has partial slots and counters for
     bool clear_counters = false;   // zero the arrival counters before a split launch
+    bool limbs = false;      // q6_K limb buffer: W = its d plane, Wexp = its H plane (L plane follows)
 };
 
 // Stream-K workspace: two 64 x 64 fp32 partial-sum slots per worker, then
@@ -79,6 +80,9 @@ int launch_quantize_tiled(const float *x, int64_t nt, int64_t id, int64_t ldx, v
 // (q4_K: d*sc and dmin*m of each of the 8 sub-blocks, in pairs; q6_K: d*sc
 // of the 16).
 int launch_prepare_q4k(const void *W, int64_t od, int64_t id, int8_t *Q, float *S, hipStream_t stream);
+// q6_K limb buffer: H plane int8 [od][id], L plane int8 [od][id], then d
+// plane fp32 [od][id/256]; v = sc * c6 = 128 H + L per element.
+int launch_prepare_q6k_limbs(const void *W, int64_t bstride, int64_t od, int64_t id, void *Wl, hipStream_t stream);
 int launch_prepare_q6k_scales(const void *W, int64_t bstride, int64_t od, int64_t id, float *S,
                               hipStream_t stream);
 

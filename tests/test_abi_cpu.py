@@ -243,3 +243,19 @@ def test_tiled_sizes_and_argument_checks():
     assert lib.mmq_q6k_q8t(A16, 224, MIS, 8, 256, B16, 4, A16, 8, None, None) == -2
     assert lib.mmq_q4k_prepared_q8t(A16, 8, 256, B16, 4, A16, 7, None, None) == -1   # ldy < od
     assert lib.mmq_q6k_prepared_q8t(MIS, 8, 256, B16, 4, A16, 8, None, None) == -2
+
+
+def test_limbs_sizes_and_argument_checks():
+    lib = qig.load()
+    assert qig.q6k_limbs_bytes(3584, 3584) == 2 * 3584 * 3584 + 3584 * 14 * 4
+    assert qig.q6k_limbs_bytes(4, 100) == 0 and qig.q6k_limbs_bytes(-1, 256) == 0
+    assert lib.prepare_q6k_limbs(A16, 200, 4, 256, B16, None) == -1       # bstride
+    assert lib.prepare_q6k_limbs(A16, 224, 4, 100, B16, None) == -1       # id % 256
+    assert lib.prepare_q6k_limbs(MIS, 224, 4, 256, B16, None) == -2
+    assert lib.prepare_q6k_limbs(A16, 224, 4, 256, MIS, None) == -2
+    assert lib.prepare_q6k_limbs(A16, 224, 0, 256, B16, None) == 0        # od == 0
+    assert lib.mmq_q6k_limbs_q8t(A16, 8, 300, B16, 4, A16, 8, None, None) == -1   # id % 256
+    assert lib.mmq_q6k_limbs_q8t(A16, 8, 256, B16, 4, A16, 7, None, None) == -1   # ldy < od
+    assert lib.mmq_q6k_limbs_q8t(MIS, 8, 256, B16, 4, A16, 8, None, None) == -2
+    assert lib.mmq_q6k_limbs_q8t(A16, 8, 256, B16, 4, A16, 8, MIS, None) == -2    # workspace
+    assert lib.mmq_q6k_limbs_q8t(A16, 8, 256, B16, 0, A16, 8, None, None) == 0    # nt == 0
