@@ -1,26 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the k-quant prefill MMQ hot path on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input at
-the q-projection shape (od = id = 3584, nt = 512):
-    quantize(x4) -> q4_K GEMM (W4)
-    quantize(x6) -> q6_K GEMM (W6, raw blocks)
-                 -> q6_K GEMM (W6, dense-plane arm)
-With --activations tiled (the default) the quantization writes the tiled
-plane (quantize_q8_tiled) and the GEMMs are the *_q8t calls; with pad40 it is
-quantize_q8_pad40 and mmq_q4k / mmq_q6k.  Both give bit-identical y; the
-other form's step is timed too and reported beside the main value.
-Inputs are resident in HBM before timing; the dense plane is built once
-beforehand (it is registration-time work) and timed separately, as are the
-prepared-buffer GEMMs (registration-time quant + fp32 scale planes), which are
-reported per kernel but are not part of the step.
+One step = one pass of the hot path over one batch of synthetic input at the
+q-projection shape (od = id = 3584, nt = 512): one q4_K and one q6_K GEMM,
+each after the quantization of its own activations into the tiled plane:
+    quantize_q8_tiled(x4) -> mmq_q4k_q8t (W4, raw blocks)
+    quantize_q8_tiled(x6) -> mmq_q6k_limbs_q8t (W6 as a limb buffer)
+Inputs are resident in HBM before timing.  Registration-time forms of the
+weights (the limb buffer, the dense plane, the prepared buffers) are built
+once beforehand and timed separately.  Every other arm -- q6_K on raw blocks
+and on the dense plane (the two paths the q6_K workload names), the prepared
+buffers, and the pad40 activation plane -- is timed per kernel after the step.
 
 Before the W warmup steps the step runs back to back for --spinup-s seconds
 (untimed), so that a short --warmup does not time a GPU that is still ramping
 its clock; the shader clock under the step's load is then measured with a
 one-wave cycle-count spin on a second stream.
 
-Prints one JSON line: value = int8 TOPS of the whole step (3 GEMMs x
+Prints one JSON line: value = int8 TOPS of the whole step (2 GEMMs x
 2*nt*od*id ops / step time), the per-kernel average durations from HIP
 events recorded on the launch stream (K launches back to back), per-launch
 medians and minima over --launches launches each, warm and cold (a 512 MiB
@@ -59,11 +56,12 @@ def parse():
     # clocks and measured up to ~10% slow, depending on what ran first
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--workload", choices=["proj", "ffn", "layer"], default="proj",
+    p.add_argument("--workload", choices=["proj", "ffn", "layer", "down"], default="proj",
                    help="proj: the q4_K and q6_K 3584x3584 nt=512 GEMMs (the headline); ffn: the 7B-class "
-                        "FFN GEMMs at nt=512; layer: all seven GEMMs of a 7B-class layer at nt=2630")
+                        "FFN GEMMs at nt=512; layer: all seven GEMMs of a 7B-class layer at nt=2630; down: "
+                        "the layer's q6_K down projection alone (3584x18944, nt=2630)")
     p.add_argument("--activations", choices=["tiled", "pad40"], default="tiled",
-                   help="activation plane of the timed step (the other form is timed and reported too)")
+                   help="ffn / layer workloads: activation plane of the timed step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy 3x (outside the timed region) so that "
                         "HBM counters taken over this run can be scaled by a kernel of known traffic")
@@ -73,8 +71,8 @@ def parse():
     p.add_argument("--launches", type=int, default=100,
                    help="launches per kernel for the per-launch medians (warm, and cold after a 512 MiB write)")
     p.add_argument("--summarize-profiles", metavar="DIR",
-                   help="instead of benchmarking: turn the rocprofv3 outputs under DIR (trace/, fetch/, write/, "
-                        "sqA/, sqB/) into the summaries under profiles/")
+                   help="instead of benchmarking: turn the rocprofv3 outputs under DIR (trace/, and for proj and "
+                        "down fetch/, write/, sqA/, sqB/) of the --workload run into the summaries under profiles/")
     return p.parse_args()
 
 
@@ -219,15 +217,14 @@ def oracle_single_thread(W4, x4, W6, x6, sample_tokens=128):
 
 
 def cpu_baseline(W4, x4, W6, x6):
-    """The oracle as it stands, on the host cores: the full step's arithmetic
-    (both quantizations and the three GEMMs), repeated until ~10 s; also the
-    mean time of each part."""
+    """The oracle as it stands, on the host cores: the step's arithmetic (both
+    quantizations, the q4_K and the q6_K GEMM), repeated until ~10 s; also the
+    mean time of each part, and single-thread times."""
     import oracle
-    ops = 3 * 2.0 * NT * OD * ID
+    ops = 2 * 2.0 * NT * OD * ID
     reps, total = 0, 0.0
-    parts = {"quantize_x4": 0.0, "mmq_q4k": 0.0, "quantize_x6": 0.0, "mmq_q6k_raw": 0.0,
-             "expand_q6k_dense": 0.0, "mmq_q6k_wexp": 0.0}
-    while total < 12.0 and reps < 200:
+    parts = {"quantize_x4": 0.0, "mmq_q4k": 0.0, "quantize_x6": 0.0, "mmq_q6k": 0.0}
+    while total < 10.0 and reps < 200:
         t = [time.perf_counter()]
         q84 = oracle.quantize_q8_pad40(x4)
         t.append(time.perf_counter())
@@ -236,10 +233,6 @@ def cpu_baseline(W4, x4, W6, x6):
         q86 = oracle.quantize_q8_pad40(x6)
         t.append(time.perf_counter())
         oracle.mmq_q6k(W6, 224, OD, ID, q86, NT)
-        t.append(time.perf_counter())
-        plane = oracle.expand_q6k_dense(W6, 224, OD, ID)
-        t.append(time.perf_counter())
-        oracle.mmq_q6k_from_plane(plane, ID, 256, W6, 224, OD, ID, q86, NT)
         t.append(time.perf_counter())
         for k, name in enumerate(parts):
             parts[name] += t[k + 1] - t[k]
@@ -250,8 +243,8 @@ def cpu_baseline(W4, x4, W6, x6):
         "unit": "TOPS",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"the full step (2 quantizations, q4_K + q6_K raw + q6_K dense-plane GEMMs, "
-                  f"nt={NT}, od=id={ID}) repeated {reps}x in {total:.1f} s",
+        "sample": f"the full step (2 quantizations, the q4_K and q6_K GEMMs, nt={NT}, od=id={ID}) "
+                  f"repeated {reps}x in {total:.1f} s",
         "parts_ms": {k: round(v / reps * 1e3, 1) for k, v in parts.items()},
         "single_thread": oracle_single_thread(W4, x4, W6, x6),
     }
@@ -268,14 +261,18 @@ GEMM_SETS = {
         ("attn_v", "q4_K", 512, 3584, "x_attn"), ("attn_o", "q4_K", 3584, 3584, "x_o"),
         ("ffn_gate", "q4_K", 18944, 3584, "x_ffn"), ("ffn_up", "q4_K", 18944, 3584, "x_ffn"),
         ("ffn_down", "q6_K", 3584, 18944, "x_down")]},
+    "down": {"nt": 2630, "xscale": 1.0, "gemms": [("ffn_down", "q6_K", 3584, 18944, "x_down")]},
 }
 CPU_SAMPLE_TOKENS = 256
 
 
 def run_gemm_set(args):
-    """The FFN or layer workload: one quantization per distinct input (tiled
-    plane, or pad40), then its GEMMs (raw blocks; the stream-K workspace is
-    passed to every GEMM and used where the tile count calls for it)."""
+    """The FFN, layer or down workload: one quantization per distinct input
+    (tiled plane, or pad40), then its GEMMs, q4_K on raw blocks and q6_K on
+    the limb buffer (tiled plane) or raw blocks (pad40); the stream-K
+    workspace is passed to every GEMM and used where the tile count calls for
+    it.  With the tiled plane each q6_K GEMM is also timed, outside the step,
+    on raw blocks and on the dense plane."""
     import torch
     import quant_integer_gemm_amd as qig
     from quant_integer_gemm_amd import inputs
@@ -284,12 +281,22 @@ def run_gemm_set(args):
     dev = torch.device("cuda:0")
     tiled = args.activations == "tiled"
     ws = qig.new_workspace(dev)
-    xs, qs, Ws, ys, host = {}, {}, {}, {}, {}
+    xs, qs, Ws, ys, host, limbs, wexps = {}, {}, {}, {}, {}, {}, {}
+    registration_us = {}
     for i, (name, qt, od, id_, xin) in enumerate(spec["gemms"]):
         W, x = inputs.make_gemm_inputs(inputs.Gemm(name, qt, od, id_, nt, spec["xscale"]),
                                        inputs.SEED_BASE + 500 + i)
         Ws[name] = torch.from_numpy(W).to(dev)
         host[name] = W
+        if qt == "q6_K" and tiled:
+            limbs[name] = torch.empty(qig.q6k_limbs_bytes(od, id_), dtype=torch.uint8, device=dev)
+            wexps[name] = torch.empty((od, id_), dtype=torch.int8, device=dev)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            qig.prepare_q6k_limbs(Ws[name], 224, od, id_, out=limbs[name])
+            torch.cuda.synchronize()
+            registration_us["prepare_q6k_limbs:" + name] = round((time.perf_counter() - t) * 1e6, 1)
+            qig.expand_q6k_dense(Ws[name], 224, od, id_, out=wexps[name])
         if xin not in xs:
             xs[xin] = torch.from_numpy(x).to(dev)
             host[xin] = x
@@ -302,17 +309,24 @@ def run_gemm_set(args):
             return lambda: qig.quantize_q8_tiled(xs[xin], out=qs[xin])
         return lambda: qig.quantize_q8_pad40(xs[xin], out=qs[xin])
 
-    def gemm(name, qt, od, id_, xin):
+    def gemm(name, qt, od, id_, xin, arm="limbs"):
         W, q8, y = Ws[name], qs[xin], ys[name]
         if qt == "q4_K":
             if tiled:
                 return lambda: qig.mmq_q4k_q8t(W, od, id_, q8, nt, y=y, ldy=od, ws=ws)
             return lambda: qig.mmq_q4k_streamk(W, od, id_, q8, nt, y=y, ldy=od, ws=ws)
-        if tiled:
-            return lambda: qig.mmq_q6k_q8t(W, 224, od, id_, q8, nt, y=y, ldy=od, ws=ws)
-        return lambda: qig.mmq_q6k_streamk(W, 224, od, id_, q8, nt, y=y, ldy=od, ws=ws)
+        if not tiled:
+            return lambda: qig.mmq_q6k_streamk(W, 224, od, id_, q8, nt, y=y, ldy=od, ws=ws)
+        if arm == "limbs":
+            Wl = limbs[name]
+            return lambda: qig.mmq_q6k_limbs_q8t(Wl, od, id_, q8, nt, y=y, ldy=od, ws=ws)
+        if arm == "wexp":
+            We = wexps[name]
+            return lambda: qig.mmq_q6k_q8t(W, 224, od, id_, q8, nt, W_exp=We, y=y, ldy=od, ws=ws)
+        return lambda: qig.mmq_q6k_q8t(W, 224, od, id_, q8, nt, y=y, ldy=od, ws=ws)
 
     names, calls, done = [], [], set()
+    extra = {}
     for (name, qt, od, id_, xin) in spec["gemms"]:
         if xin not in done:
             names.append("quantize_" + xin)
@@ -320,6 +334,9 @@ def run_gemm_set(args):
             done.add(xin)
         names.append(name)
         calls.append(gemm(name, qt, od, id_, xin))
+        if qt == "q6_K" and tiled:
+            extra[name + "[raw]"] = gemm(name, qt, od, id_, xin, "raw")
+            extra[name + "[wexp]"] = gemm(name, qt, od, id_, xin, "wexp")
 
     def step():
         for fn in calls:
@@ -336,8 +353,17 @@ def run_gemm_set(args):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     per = {}
-    for n, fn in zip(names, calls):
+    for n, fn in list(zip(names, calls)) + list(extra.items()):
+        fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -346,6 +372,8 @@ def run_gemm_set(args):
         torch.cuda.synchronize()
         per[n] = e0.elapsed_time(e1) * 1e3 / args.steps
     ops = {name: 2.0 * nt * od * id_ for (name, qt, od, id_, xin) in spec["gemms"]}
+    for n in extra:
+        ops[n] = ops[n.split("[")[0]]
     total_ops = sum(ops.values())
     gemms = [g[0] for g in spec["gemms"]]
     dom = max(gemms, key=lambda n: per[n])
@@ -364,16 +392,19 @@ def run_gemm_set(args):
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": ("7B-class FFN GEMMs at nt=512: q4_K gate/up 18944x3584, q6_K down 3584x18944"
-                         if args.workload == "ffn" else
-                         "7B-class layer at nt=2630: q4_K q, k, v, o, gate, up and q6_K down, one "
-                         "quantization per distinct input"),
+            "workload": {"ffn": "7B-class FFN GEMMs at nt=512: q4_K gate/up 18944x3584, q6_K down 3584x18944",
+                         "layer": "7B-class layer at nt=2630: q4_K q, k, v, o, gate, up and q6_K down, one "
+                                  "quantization per distinct input",
+                         "down": "7B-class layer's q6_K down projection 3584x18944 at nt=2630, after its "
+                                 "activation quantization"}[args.workload],
+            "q6k_arm": "limbs" if tiled else "raw",
             "activations": args.activations, "nt": nt,
             "gemms": {g[0]: f"{g[1]} {g[2]}x{g[3]}" for g in spec["gemms"]},
         },
         "per_kernel_us": {k: round(v, 3) for k, v in per.items()},
-        "summed_us": round(sum(per.values()), 2),
-        "per_gemm_tops": {n: round(ops[n] / (per[n] * 1e-6) / 1e12, 1) for n in gemms},
+        "summed_us": round(sum(per[n] for n in names), 2),
+        "per_gemm_tops": {n: round(ops[n] / (per[n] * 1e-6) / 1e12, 1) for n in gemms + list(extra)},
+        "registration_us": registration_us,
         "spinup": {"seconds": args.spinup_s, "steps": spun},
         "clocks_mhz": clocks,
         "roofline": {
@@ -421,28 +452,43 @@ PROFILE_NAMES = {
     "qig::mmq_kernel<6, 2, 0, 0>": "mmq_q6k_prepared", "qig::mmq_kernel<4, 0, 0, 1>": "mmq_q4k_q8t",
     "qig::mmq_kernel<6, 0, 0, 1>": "mmq_q6k_raw_q8t", "qig::mmq_kernel<6, 1, 0, 1>": "mmq_q6k_wexp_q8t",
     "qig::mmq_kernel<4, 2, 0, 1>": "mmq_q4k_prepared_q8t", "qig::mmq_kernel<6, 2, 0, 1>": "mmq_q6k_prepared_q8t",
+    "qig::mmq_limbs_kernel": "mmq_q6k_limbs_q8t",
     "qig::prepare_q4k_kernel": "prepare_q4k", "qig::prepare_q6k_scales_kernel": "prepare_q6k (scales)",
+    "qig::prepare_q6k_limbs_kernel": "prepare_q6k_limbs",
     "qig::quantize_kernel": "quantize_q8_pad40", "qig::quantize_tiled_kernel<1>": "quantize_q8_tiled",
     "qig::quantize_tiled_kernel<2>": "quantize_q8_tiled (2 tokens per group)",
-    "qig::expand_q6k_kernel": "expand_q6k_dense", "__amd_rocclr_copyBuffer": "copy_256MiB (calibration)",
+    "qig::expand_q6k_kernel": "expand_q6k_dense", "qig::clear_counters_kernel": "clear_counters",
+    "__amd_rocclr_copyBuffer": "copy_256MiB (calibration)",
+}
+# shapes (nt, od, id) and titles of the profiled workloads
+PROFILE_WORKLOADS = {
+    "proj": (512, 3584, 3584, "mmq_3584x3584_nt512",
+             "q4_K / q6_K MMQ at od=id=3584, nt=512 (bench.py default run)"),
+    "down": (2630, 3584, 18944, "mmq_q6k_down_3584x18944_nt2630",
+             "q6_K down projection MMQ at od=3584, id=18944, nt=2630 (bench.py --workload down)"),
+    "layer": (2630, None, None, "mmq_layer_nt2630",
+              "the seven GEMMs of a 7B-class layer at nt=2630 (bench.py --workload layer)"),
 }
 
 
-def _algorithmic_bytes():
-    """(read, write) bytes of one launch of each kernel at od = id = 3584,
-    nt = 512: each input and output once."""
-    nsb, q8 = ID // 256, NT * (ID // 32) * 40
-    y = NT * OD * 4
-    raw4, raw6 = OD * nsb * 144, OD * nsb * 224
-    wexp = OD * ID + OD * nsb * 18
-    prep4, prep6 = OD * ID // 2 + OD * nsb * 64, OD * ID + OD * nsb * 64
+def _algorithmic_bytes(nt=NT, od=OD, id_=ID):
+    """(read, write) bytes of one launch of each kernel at the given shape:
+    each input and output once."""
+    nsb, q8 = id_ // 256, nt * (id_ // 32) * 40
+    y = nt * od * 4
+    raw4, raw6 = od * nsb * 144, od * nsb * 224
+    wexp = od * id_ + od * nsb * 18
+    prep4, prep6 = od * id_ // 2 + od * nsb * 64, od * id_ + od * nsb * 64
+    limbs = 2 * od * id_ + od * nsb * 4
     gemm = {"mmq_q4k": raw4, "mmq_q6k_raw": raw6, "mmq_q6k_wexp": wexp, "mmq_q4k_prepared": prep4,
             "mmq_q6k_prepared": prep6}
     alg = {}
     for k, w in gemm.items():
         alg[k] = alg[k + "_q8t"] = (w + q8, y)
-    alg["quantize_q8_pad40"] = alg["quantize_q8_tiled"] = (NT * ID * 4, q8)
-    alg["expand_q6k_dense"] = (OD * nsb * 210, OD * ID)
+    alg["mmq_q6k_limbs_q8t"] = (limbs + q8, y)
+    alg["quantize_q8_pad40"] = alg["quantize_q8_tiled"] = (nt * id_ * 4, q8)
+    alg["expand_q6k_dense"] = (od * nsb * 210, od * id_)
+    alg["prepare_q6k_limbs"] = (od * nsb * 210, limbs)
     alg["copy_256MiB (calibration)"] = (256 << 20, 256 << 20)
     return alg
 
@@ -454,43 +500,58 @@ COUNTER_SETS = [
     ("sqB", "SQ_INSTS_VALU_MFMA_MOPS_I8 SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_INSTS_SALU "
             "SQ_WAIT_INST_LDS SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE"),
 ]
-PROFILE_BENCH = "python3 /root/repo/bench.py --steps 5 --warmup 2 --launches 5 --no-cpu-baseline --copy-calibration"
+PROFILE_BENCH = {
+    "proj": "python3 /root/repo/bench.py --steps 5 --warmup 2 --launches 5 --no-cpu-baseline --copy-calibration",
+    "down": "python3 /root/repo/bench.py --workload down --steps 5 --warmup 2 --no-cpu-baseline "
+            "--copy-calibration",
+}
+PROFILE_TRACE = {
+    "proj": "python3 /root/repo/bench.py",
+    "down": "python3 /root/repo/bench.py --workload down --no-cpu-baseline",
+    "layer": "python3 /root/repo/bench.py --workload layer --no-cpu-baseline",
+}
 
 
-def summarize_profiles(src_dir):
-    """Write profiles/mmq_3584x3584_nt512_{kernel_trace,counters}.md and
-    profiles/mmq_traffic.json from rocprofv3 outputs under src_dir:
-    trace/t_kernel_trace.csv (kernel trace of the default bench run, whose
+def summarize_profiles(src_dir, workload="proj", out_dir=None):
+    """Write profiles/<tag>_{kernel_trace,counters}.md (and, for the proj
+    workload, profiles/mmq_traffic.json) from rocprofv3 outputs under src_dir:
+    trace/t_kernel_trace.csv (kernel trace of the PROFILE_TRACE run, whose
     bench line is trace/bench.json) and {fetch,write,sqA,sqB}/p_counter_collection.csv
     (one counter run each, of PROFILE_BENCH)."""
     import collections
     import csv
 
     def short(k):
-        return k.replace("void ", "").split("(")[0]
+        return k.replace("(anonymous namespace)", "{anon}").replace("void ", "").split("(")[0]
 
-    tag = "mmq_3584x3584_nt512"
-    out_dir = os.path.join(ROOT, "profiles")
+    nt, od, id_, tag, title = PROFILE_WORKLOADS[workload]
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
     # --- kernel trace
     disp = collections.defaultdict(list)
     for r in csv.DictReader(open(os.path.join(src_dir, "trace", "t_kernel_trace.csv"))):
-        disp[short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        disp[(short(r["Kernel_Name"]), wg)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     total = sum(sum(v) for v in disp.values())
-    tl = ["# Kernel trace: bench.py default run (q4_K / q6_K MMQ at od=id=3584, nt=512)", "",
+    tl = [f"# Kernel trace: {title}", "",
           "Command, from /tmp (`cd /tmp && export TMPDIR=/tmp`):", "```",
           "timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/trace -o t "
-          "-- python3 /root/repo/bench.py", "```", "",
-          "Per-dispatch durations of every launch in the run: the spin-up and warmup steps, the timed steps, "
-          "the back-to-back launches behind bench.py's per-kernel averages, and 100 warm and 100 cold (after a "
-          "512 MiB write) launches per step kernel. The median is the steady warm figure; `mean` includes the "
-          "cold launches and the clock ramp at the start.", "",
-          "| kernel | calls | median us | mean us | p10 us | min us | max us | share of GPU time |",
-          "|---|---|---|---|---|---|---|---|"]
-    for k, d in sorted(disp.items(), key=lambda kv: -sum(kv[1])):
+          f"-- {PROFILE_TRACE[workload]}", "```", "",
+          ("Per-dispatch durations of every launch in the run: the spin-up and warmup steps, the timed steps, "
+           "the back-to-back launches behind bench.py's per-kernel averages, and 100 warm and 100 cold (after a "
+           "512 MiB write) launches per step kernel. The median is the steady warm figure; `mean` includes the "
+           "cold launches and the clock ramp at the start." if workload == "proj" else
+           "Per-dispatch durations of every launch in the run: the spin-up and warmup steps, the timed steps, "
+           "and the back-to-back launches behind bench.py's per-kernel averages, which also time the q6_K GEMM "
+           "on raw blocks and on the dense plane. The median is the steady figure."), "",
+          "Dispatches are grouped by kernel and workgroup count (GEMMs of different shapes, and whole-tile "
+          "and split launches, differ in it).", "",
+          "| kernel | workgroups | calls | median us | mean us | p10 us | min us | max us | share of GPU time |",
+          "|---|---|---|---|---|---|---|---|---|"]
+    for (k, wg), d in sorted(disp.items(), key=lambda kv: -sum(kv[1])):
         d = sorted(d)
         n = PROFILE_NAMES.get(k, k)
-        tl.append(f"| {n} | {len(d)} | {d[len(d) // 2]:.2f} | {sum(d) / len(d):.2f} | {d[len(d) // 10]:.2f} | "
-                  f"{d[0]:.2f} | {d[-1]:.2f} | {100 * sum(d) / total:.1f}% |")
+        tl.append(f"| {n} | {wg} | {len(d)} | {d[len(d) // 2]:.2f} | {sum(d) / len(d):.2f} | "
+                  f"{d[len(d) // 10]:.2f} | {d[0]:.2f} | {d[-1]:.2f} | {100 * sum(d) / total:.1f}% |")
     bj = os.path.join(src_dir, "trace", "bench.json")
     if os.path.exists(bj):
         tl += ["", "The same run's bench.py line (per-kernel figures from HIP events on the launch stream):", "```",
@@ -498,6 +559,8 @@ def summarize_profiles(src_dir):
     with open(os.path.join(out_dir, f"{tag}_kernel_trace.md"), "w") as f:
         f.write("\n".join(tl) + "\n")
     # --- counters
+    if od is None:
+        return
     cnt = collections.defaultdict(dict)
     for sub, _ in COUNTER_SETS:
         path = os.path.join(src_dir, sub, "p_counter_collection.csv")
@@ -514,12 +577,12 @@ def summarize_profiles(src_dir):
         return
     fs = copy["FETCH_SIZE"] * 1024 / (256 << 20)
     wsc = copy["WRITE_SIZE"] * 1024 / (256 << 20)
-    alg = _algorithmic_bytes()
-    lines = ["# HBM traffic and SQ counters: q4_K / q6_K MMQ at od=id=3584, nt=512", "",
+    alg = _algorithmic_bytes(nt, od, id_)
+    lines = [f"# HBM traffic and SQ counters: {title}", "",
              "Each counter set is its own run, from /tmp (`cd /tmp && export TMPDIR=/tmp`):", "```"]
     for sub, cs in COUNTER_SETS:
         lines.append(f"timeout -s KILL 120 rocprofv3 --pmc {cs} --output-format csv -d gpurun_out/prof/{sub} -o p "
-                     f"-- {PROFILE_BENCH}")
+                     f"-- {PROFILE_BENCH[workload]}")
     lines += ["```", "",
               f"Calibration: a plain 256 MiB device copy reads FETCH_SIZE = {copy['FETCH_SIZE']:.0f} KiB and "
               f"WRITE_SIZE = {copy['WRITE_SIZE']:.0f} KiB per dispatch against 262144 KiB moved each way, so HBM "
@@ -549,6 +612,8 @@ def summarize_profiles(src_dir):
         lines.append(f"| {n} | " + " | ".join(f"{c[x]:.0f}" if x in c else "—" for x in cols) + " |")
     with open(os.path.join(out_dir, f"{tag}_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    if workload != "proj":
+        return
     rec = {"kernel_code_sha256": kernel_source_digest(), "fetch_scale": round(fs, 5), "write_scale": round(wsc, 5),
            "source": f"profiles/{tag}_counters.md",
            "bytes_per_launch": {k: v for k, v in traffic.items() if k.startswith("mmq")}}
@@ -559,7 +624,7 @@ def summarize_profiles(src_dir):
 def main():
     args = parse()
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles)
+        summarize_profiles(args.summarize_profiles, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -591,10 +656,10 @@ def main():
     t86 = torch.empty(qig.q8_tiled_bytes(NT, ID), dtype=torch.uint8, device=dev)
     y4 = torch.empty((NT, OD), dtype=torch.float32, device=dev)
     y6 = torch.empty((NT, OD), dtype=torch.float32, device=dev)
-    y6e = torch.empty((NT, OD), dtype=torch.float32, device=dev)
     wexp = torch.empty((OD, ID), dtype=torch.int8, device=dev)
     W4p = torch.empty(qig.prepared_bytes("q4_K", OD, ID), dtype=torch.uint8, device=dev)
     W6p = torch.empty(qig.prepared_bytes("q6_K", OD, ID), dtype=torch.uint8, device=dev)
+    W6l = torch.empty(qig.q6k_limbs_bytes(OD, ID), dtype=torch.uint8, device=dev)
 
     # registration-time work, each timed on its own
     def time_us(fn, reps=10):
@@ -612,30 +677,34 @@ def main():
         "expand_q6k_dense": time_us(lambda: qig.expand_q6k_dense(W6d, 224, OD, ID, out=wexp)),
         "prepare_q4k": time_us(lambda: qig.prepare_q4k(W4d, OD, ID, out=W4p)),
         "prepare_q6k": time_us(lambda: qig.prepare_q6k(W6d, 224, OD, ID, out=W6p)),
+        "prepare_q6k_limbs": time_us(lambda: qig.prepare_q6k_limbs(W6d, 224, OD, ID, out=W6l)),
     }
-    y4p = torch.empty((NT, OD), dtype=torch.float32, device=dev)
-    y6p = torch.empty((NT, OD), dtype=torch.float32, device=dev)
 
+    # The step: one q4_K and one q6_K GEMM at the q-projection shape, each after
+    # its activation quantization (tiled plane); the q6_K GEMM runs on the limb
+    # buffer, the fastest q6_K arm.  Every other arm and activation form is
+    # timed after it, per kernel.
     steps = {
-        "pad40": {
-            "quantize_x4": lambda: qig.quantize_q8_pad40(x4d, out=q84),
-            "mmq_q4k": lambda: qig.mmq_q4k(W4d, OD, ID, q84, NT, y=y4, ldy=OD),
-            "quantize_x6": lambda: qig.quantize_q8_pad40(x6d, out=q86),
-            "mmq_q6k_raw": lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, y=y6, ldy=OD),
-            "mmq_q6k_wexp": lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, W_exp=wexp, y=y6e, ldy=OD),
-        },
-        "tiled": {
-            "quantize_tiled_x4": lambda: qig.quantize_q8_tiled(x4d, out=t84),
-            "mmq_q4k_q8t": lambda: qig.mmq_q4k_q8t(W4d, OD, ID, t84, NT, y=y4, ldy=OD),
-            "quantize_tiled_x6": lambda: qig.quantize_q8_tiled(x6d, out=t86),
-            "mmq_q6k_raw_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, y=y6, ldy=OD),
-            "mmq_q6k_wexp_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, W_exp=wexp, y=y6e, ldy=OD),
-        },
+        "quantize_tiled_x4": lambda: qig.quantize_q8_tiled(x4d, out=t84),
+        "mmq_q4k_q8t": lambda: qig.mmq_q4k_q8t(W4d, OD, ID, t84, NT, y=y4, ldy=OD),
+        "quantize_tiled_x6": lambda: qig.quantize_q8_tiled(x6d, out=t86),
+        "mmq_q6k_limbs_q8t": lambda: qig.mmq_q6k_limbs_q8t(W6l, OD, ID, t86, NT, y=y6, ldy=OD),
     }
-    main_form = args.activations
-    other_form = "pad40" if main_form == "tiled" else "tiled"
-    names = list(steps[main_form])
-    calls = list(steps[main_form].values())
+    arms = {
+        "mmq_q6k_raw_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, y=y6, ldy=OD),
+        "mmq_q6k_wexp_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, W_exp=wexp, y=y6, ldy=OD),
+        "mmq_q6k_prepared_q8t": lambda: qig.mmq_q6k_prepared_q8t(W6p, OD, ID, t86, NT, y=y6, ldy=OD),
+        "mmq_q4k_prepared_q8t": lambda: qig.mmq_q4k_prepared_q8t(W4p, OD, ID, t84, NT, y=y4, ldy=OD),
+        "quantize_x4": lambda: qig.quantize_q8_pad40(x4d, out=q84),
+        "quantize_x6": lambda: qig.quantize_q8_pad40(x6d, out=q86),
+        "mmq_q4k": lambda: qig.mmq_q4k(W4d, OD, ID, q84, NT, y=y4, ldy=OD),
+        "mmq_q6k_raw": lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, y=y6, ldy=OD),
+        "mmq_q6k_wexp": lambda: qig.mmq_q6k(W6d, 224, OD, ID, q86, NT, W_exp=wexp, y=y6, ldy=OD),
+        "mmq_q4k_prepared": lambda: qig.mmq_q4k_prepared(W4p, OD, ID, q84, NT, y=y4, ldy=OD),
+        "mmq_q6k_prepared": lambda: qig.mmq_q6k_prepared(W6p, OD, ID, q86, NT, y=y6, ldy=OD),
+    }
+    names = list(steps)
+    calls = list(steps.values())
 
     def step():
         for fn in calls:
@@ -654,20 +723,6 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # the other activation form's step, timed the same way first (after its own
-    # warmup), so that neither form is timed on a colder GPU than the other
-    other_calls = list(steps[other_form].values())
-    for _ in range(args.warmup):
-        for fn in other_calls:
-            fn()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        for fn in other_calls:
-            fn()
-    torch.cuda.synchronize()
-    ms_other = (time.perf_counter() - t0) / args.steps * 1e3
-
     # timed region: K whole steps back to back
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -681,7 +736,8 @@ def main():
     # pair of HIP events recorded on the launch stream (an event pair around
     # every single launch would add the event's own latency to each figure)
     per = {}
-    for n, fn in list(steps[main_form].items()) + list(steps[other_form].items()):
+    for n, fn in list(steps.items()) + list(arms.items()):
+        fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -696,29 +752,25 @@ def main():
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     event_overhead = per_launch_us(lambda: tiny.add_(1.0), args.launches)
     per_launch = {}
-    for n, fn in steps[main_form].items():
+    for n, fn in steps.items():
         per_launch[n] = {"warm": per_launch_us(fn, args.launches),
                          "cold": per_launch_us(fn, args.launches, flush=lambda k: flush_buf.fill_(k & 255))}
     del flush_buf
-    # the prepared-buffer arms (not part of the step), timed the same way
-    extra = {"mmq_q4k_prepared": lambda: qig.mmq_q4k_prepared(W4p, OD, ID, q84, NT, y=y4p, ldy=OD),
-             "mmq_q6k_prepared": lambda: qig.mmq_q6k_prepared(W6p, OD, ID, q86, NT, y=y6p, ldy=OD),
-             "mmq_q4k_prepared_q8t": lambda: qig.mmq_q4k_prepared_q8t(W4p, OD, ID, t84, NT, y=y4p, ldy=OD),
-             "mmq_q6k_prepared_q8t": lambda: qig.mmq_q6k_prepared_q8t(W6p, OD, ID, t86, NT, y=y6p, ldy=OD)}
-    for n, fn in extra.items():
-        per[n] = time_us(fn, reps=args.steps)
 
     gemm_ops = 2.0 * NT * OD * ID
-    value = 3 * gemm_ops / (ms_per_step * 1e-3) / 1e12
+    value = 2 * gemm_ops / (ms_per_step * 1e-3) / 1e12
     gemms = [n for n in names if n.startswith("mmq")]
-    all_gemms = gemms + [n for n in steps[other_form] if n.startswith("mmq")]
+    all_gemms = gemms + [n for n in arms if n.startswith("mmq")]
     dom = max(gemms, key=lambda n: per[n])
     achieved = gemm_ops / (per[dom] * 1e-6) / 1e12
-    # algorithmic bytes per launch of each GEMM: weights (raw blocks; for the dense-plane arm
-    # the plane plus d and the 16 scales of each block) + pad40 plane + fp32 y, once each
-    # (the tiled plane has the pad40 plane's size at this nt)
-    wb = {"mmq_q4k": OD * (ID // 256) * 144, "mmq_q6k_raw": OD * (ID // 256) * 224,
-          "mmq_q6k_wexp": OD * ID + OD * (ID // 256) * 18}
+    # algorithmic bytes per launch of each GEMM: its weight form (raw blocks; the
+    # dense plane plus d and the 16 scales of each block; a prepared or limb
+    # buffer) + the activation plane + fp32 y, once each (the tiled plane has
+    # the pad40 plane's size at this nt)
+    nsb = ID // 256
+    wb = {"mmq_q4k": OD * nsb * 144, "mmq_q6k_raw": OD * nsb * 224, "mmq_q6k_wexp": OD * ID + OD * nsb * 18,
+          "mmq_q4k_prepared": qig.prepared_bytes("q4_K", OD, ID), "mmq_q6k_prepared": qig.prepared_bytes("q6_K", OD, ID),
+          "mmq_q6k_limbs": qig.q6k_limbs_bytes(OD, ID)}
     wbytes = {n: wb[n.replace("_q8t", "")] for n in all_gemms}
     abytes = nb + NT * OD * 4
     dom_bytes = wbytes[dom] + abytes
@@ -737,15 +789,13 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "q4_K + q6_K GEMMs od=id=3584, nt=512 (quantize, q4_K GEMM, q6_K GEMM raw, "
-                        "q6_K GEMM dense-plane arm)",
-            "activations": main_form,
+            "workload": "q4_K GEMM and q6_K GEMM, od=id=3584, nt=512, each after its activation quantization "
+                        "(tiled plane); q6_K on the registration-time limb buffer; the raw-block, dense-plane "
+                        "and prepared q6_K arms timed per kernel",
             "nt": NT, "od": OD, "id": ID, "seeds": [SEED4, SEED6],
         },
         "per_kernel_us": {k: round(v, 3) for k, v in per.items()},
-        "other_activations": {"activations": other_form, "value": round(3 * gemm_ops / (ms_other * 1e-3) / 1e12, 2),
-                              "ms_per_step": round(ms_other, 4)},
-        "per_gemm_tops": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12, 1) for n in all_gemms + list(extra)},
+        "per_gemm_tops": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12, 1) for n in all_gemms},
         "per_gemm_pct_int8_peak": {n: round(100 * gemm_ops / (per[n] * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2)
                                    for n in all_gemms},
         "per_gemm_hbm_gbs": {n: round((wbytes[n] + abytes) / (per[n] * 1e-6) / 1e9, 1) for n in all_gemms},
@@ -769,6 +819,8 @@ def main():
             "hbm_peak_gbs": PEAK_HBM_GBS,
             "hbm_frac": round(dom_bytes / (per[dom] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         },
+        "roofline_frac_per_arm": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)
+                                  for n in all_gemms},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W4, x4, W6, x6)
