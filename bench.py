@@ -19,9 +19,10 @@ one-wave cycle-count spin on a second stream.
 
 Prints one JSON line: value = int8 TOPS of the whole step (2 GEMMs x
 2*nt*od*id ops / step time), the per-kernel average durations from HIP
-events recorded on the launch stream (K launches back to back), per-launch
-medians and minima over --launches launches each, warm and cold (a 512 MiB
-write before each launch), a roofline entry for the dominant kernel against
+events recorded on the launch stream (K launches queued back to back
+behind a spin kernel, so that a kernel shorter than the host's launch time
+is still timed on the GPU), per-launch medians and minima over --launches
+launches each, warm and cold (a 512 MiB write before each launch), a roofline entry for the dominant kernel against
 the int8 MFMA peak (also at the measured clock) and against HBM, and the CPU
 oracle timed on the host cores.
 
@@ -56,10 +57,11 @@ def parse():
     # clocks and measured up to ~10% slow, depending on what ran first
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--workload", choices=["proj", "ffn", "layer", "down"], default="proj",
+    p.add_argument("--workload", choices=["proj", "ffn", "layer", "down", "kv"], default="proj",
                    help="proj: the q4_K and q6_K 3584x3584 nt=512 GEMMs (the headline); ffn: the 7B-class "
                         "FFN GEMMs at nt=512; layer: all seven GEMMs of a 7B-class layer at nt=2630; down: "
-                        "the layer's q6_K down projection alone (3584x18944, nt=2630)")
+                        "the layer's q6_K down projection alone (3584x18944, nt=2630); kv: the layer's k and v "
+                        "projections")
     p.add_argument("--activations", choices=["tiled", "pad40"], default="tiled",
                    help="ffn / layer workloads: activation plane of the timed step")
     p.add_argument("--copy-calibration", action="store_true",
@@ -76,7 +78,7 @@ def parse():
     return p.parse_args()
 
 
-KERNEL_SOURCES = ("mmq.hip", "qig_device.h", "qig_launch.h")
+KERNEL_SOURCES = ("mmq.hip", "qig_device.h", "qig_launch.h", "qig_quant.h")
 
 
 def kernel_source_digest() -> str:
@@ -169,19 +171,58 @@ def spin_up(step, seconds):
                "smi_mhz": smi[len(smi) // 2] if smi else None}
 
 
+def queue_ahead(host_seconds):
+    """Occupy the launch stream for about 1.5x `host_seconds` with a spin
+    kernel, so that launches the host queues meanwhile run back to back once
+    it ends: HIP events around them then time the GPU, not the host's launch
+    rate (a short kernel finishes before the host has queued the next)."""
+    import torch
+    torch.cuda._sleep(int(1.5 * host_seconds * 2.6e9) + (1 << 16))
+
+
+def gpu_avg_us(fn, n):
+    """Average duration of fn over n launches queued back to back behind a
+    spin kernel, between one pair of HIP events on the launch stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(n):
+        fn()
+    host = time.perf_counter() - t
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    queue_ahead(host)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
 def per_launch_us(fn, n, flush=None):
     """Median and minimum of n launches of fn, each between its own pair of
-    HIP events on the launch stream; with `flush`, a write of 512 MiB (which
-    evicts the L2s and the 256 MB Infinity Cache) runs before each launch,
-    outside its events."""
+    HIP events on the launch stream, all queued behind a spin kernel; with
+    `flush`, a write of 512 MiB (which evicts the L2s and the 256 MB Infinity
+    Cache) runs before each launch, outside its events."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for k, (e0, e1) in enumerate(evs):
-        if flush is not None:
-            flush(k)
-        e0.record()
-        fn()
-        e1.record()
+
+    def batch():
+        for k, (e0, e1) in enumerate(evs):
+            if flush is not None:
+                flush(k)
+            e0.record()
+            fn()
+            e1.record()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    batch()
+    host = time.perf_counter() - t
+    torch.cuda.synchronize()
+    queue_ahead(host)
+    batch()
     torch.cuda.synchronize()
     ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
     return {"median": round(ts[len(ts) // 2], 3), "min": round(ts[0], 3)}
@@ -262,6 +303,8 @@ GEMM_SETS = {
         ("ffn_gate", "q4_K", 18944, 3584, "x_ffn"), ("ffn_up", "q4_K", 18944, 3584, "x_ffn"),
         ("ffn_down", "q6_K", 3584, 18944, "x_down")]},
     "down": {"nt": 2630, "xscale": 1.0, "gemms": [("ffn_down", "q6_K", 3584, 18944, "x_down")]},
+    "kv": {"nt": 2630, "xscale": 1.0, "gemms": [
+        ("attn_k", "q4_K", 512, 3584, "x_attn"), ("attn_v", "q4_K", 512, 3584, "x_attn")]},
 }
 CPU_SAMPLE_TOKENS = 256
 
@@ -337,6 +380,10 @@ def run_gemm_set(args):
         if qt == "q6_K" and tiled:
             extra[name + "[raw]"] = gemm(name, qt, od, id_, xin, "raw")
             extra[name + "[wexp]"] = gemm(name, qt, od, id_, xin, "wexp")
+        if qt == "q4_K" and tiled:
+            # the same GEMM quantizing its own activations (no q8 plane)
+            extra[name + "[xf32]"] = (lambda W=Ws[name], x=xs[xin], y=ys[name], od=od, id_=id_:
+                                      qig.mmq_q4k_xf32(W, od, id_, x, y=y, ldy=od, ws=ws))
 
     def step():
         for fn in calls:
@@ -361,16 +408,7 @@ def run_gemm_set(args):
         torch.cuda.synchronize()
         del src, dst
 
-    per = {}
-    for n, fn in list(zip(names, calls)) + list(extra.items()):
-        fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        per[n] = e0.elapsed_time(e1) * 1e3 / args.steps
+    per = {n: gpu_avg_us(fn, args.steps) for n, fn in list(zip(names, calls)) + list(extra.items())}
     ops = {name: 2.0 * nt * od * id_ for (name, qt, od, id_, xin) in spec["gemms"]}
     for n in extra:
         ops[n] = ops[n.split("[")[0]]
@@ -396,7 +434,9 @@ def run_gemm_set(args):
                          "layer": "7B-class layer at nt=2630: q4_K q, k, v, o, gate, up and q6_K down, one "
                                   "quantization per distinct input",
                          "down": "7B-class layer's q6_K down projection 3584x18944 at nt=2630, after its "
-                                 "activation quantization"}[args.workload],
+                                 "activation quantization",
+                         "kv": "7B-class layer's q4_K k and v projections 512x3584 at nt=2630 after one "
+                               "shared activation quantization"}[args.workload],
             "q6k_arm": "limbs" if tiled else "raw",
             "activations": args.activations, "nt": nt,
             "gemms": {g[0]: f"{g[1]} {g[2]}x{g[3]}" for g in spec["gemms"]},
@@ -452,7 +492,7 @@ PROFILE_NAMES = {
     "qig::mmq_kernel<6, 2, 0, 0>": "mmq_q6k_prepared", "qig::mmq_kernel<4, 0, 0, 1>": "mmq_q4k_q8t",
     "qig::mmq_kernel<6, 0, 0, 1>": "mmq_q6k_raw_q8t", "qig::mmq_kernel<6, 1, 0, 1>": "mmq_q6k_wexp_q8t",
     "qig::mmq_kernel<4, 2, 0, 1>": "mmq_q4k_prepared_q8t", "qig::mmq_kernel<6, 2, 0, 1>": "mmq_q6k_prepared_q8t",
-    "qig::mmq_limbs_kernel": "mmq_q6k_limbs_q8t",
+    "qig::mmq_limbs_kernel": "mmq_q6k_limbs_q8t", "qig::mmq_kernel<4, 0, 0, 2>": "mmq_q4k_xf32",
     "qig::prepare_q4k_kernel": "prepare_q4k", "qig::prepare_q6k_scales_kernel": "prepare_q6k (scales)",
     "qig::prepare_q6k_limbs_kernel": "prepare_q6k_limbs",
     "qig::quantize_kernel": "quantize_q8_pad40", "qig::quantize_tiled_kernel<1>": "quantize_q8_tiled",
@@ -486,6 +526,7 @@ def _algorithmic_bytes(nt=NT, od=OD, id_=ID):
     for k, w in gemm.items():
         alg[k] = alg[k + "_q8t"] = (w + q8, y)
     alg["mmq_q6k_limbs_q8t"] = (limbs + q8, y)
+    alg["mmq_q4k_xf32"] = (raw4 + nt * id_ * 4, y)
     alg["quantize_q8_pad40"] = alg["quantize_q8_tiled"] = (nt * id_ * 4, q8)
     alg["expand_q6k_dense"] = (od * nsb * 210, od * id_)
     alg["prepare_q6k_limbs"] = (od * nsb * 210, limbs)
@@ -691,6 +732,7 @@ def main():
         "mmq_q6k_limbs_q8t": lambda: qig.mmq_q6k_limbs_q8t(W6l, OD, ID, t86, NT, y=y6, ldy=OD),
     }
     arms = {
+        "mmq_q4k_xf32": lambda: qig.mmq_q4k_xf32(W4d, OD, ID, x4d, y=y4, ldy=OD),
         "mmq_q6k_raw_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, y=y6, ldy=OD),
         "mmq_q6k_wexp_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, W_exp=wexp, y=y6, ldy=OD),
         "mmq_q6k_prepared_q8t": lambda: qig.mmq_q6k_prepared_q8t(W6p, OD, ID, t86, NT, y=y6, ldy=OD),
@@ -732,19 +774,11 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
 
-    # per-kernel durations: each call launched K times back to back between one
-    # pair of HIP events recorded on the launch stream (an event pair around
-    # every single launch would add the event's own latency to each figure)
-    per = {}
-    for n, fn in list(steps.items()) + list(arms.items()):
-        fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        per[n] = e0.elapsed_time(e1) * 1e3 / args.steps
+    # per-kernel durations: each call launched K times back to back, queued
+    # behind a spin kernel, between one pair of HIP events recorded on the
+    # launch stream (an event pair around every single launch would add the
+    # event's own latency to each figure)
+    per = {n: gpu_avg_us(fn, args.steps) for n, fn in list(steps.items()) + list(arms.items())}
     # per-launch distributions of the step's kernels: warm (back to back) and
     # cold (a 512 MiB write before each launch, outside its events), against
     # the same event pair around a one-element kernel
@@ -770,10 +804,12 @@ def main():
     nsb = ID // 256
     wb = {"mmq_q4k": OD * nsb * 144, "mmq_q6k_raw": OD * nsb * 224, "mmq_q6k_wexp": OD * ID + OD * nsb * 18,
           "mmq_q4k_prepared": qig.prepared_bytes("q4_K", OD, ID), "mmq_q6k_prepared": qig.prepared_bytes("q6_K", OD, ID),
-          "mmq_q6k_limbs": qig.q6k_limbs_bytes(OD, ID)}
+          "mmq_q6k_limbs": qig.q6k_limbs_bytes(OD, ID), "mmq_q4k_xf32": OD * nsb * 144}
     wbytes = {n: wb[n.replace("_q8t", "")] for n in all_gemms}
     abytes = nb + NT * OD * 4
-    dom_bytes = wbytes[dom] + abytes
+    # the fused GEMM reads the fp32 activations in place of a q8 plane
+    gbytes = {n: wbytes[n] + (NT * ID * 4 + NT * OD * 4 if n.endswith("xf32") else abytes) for n in all_gemms}
+    dom_bytes = gbytes[dom]
     clock_frac = None if clock_mhz is None else round(achieved / (PEAK_INT8_TOPS * clock_mhz / 2400.0), 4)
     out = {
         "metric": METRIC,
@@ -798,7 +834,7 @@ def main():
         "per_gemm_tops": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12, 1) for n in all_gemms},
         "per_gemm_pct_int8_peak": {n: round(100 * gemm_ops / (per[n] * 1e-6) / 1e12 / PEAK_INT8_TOPS, 2)
                                    for n in all_gemms},
-        "per_gemm_hbm_gbs": {n: round((wbytes[n] + abytes) / (per[n] * 1e-6) / 1e9, 1) for n in all_gemms},
+        "per_gemm_hbm_gbs": {n: round(gbytes[n] / (per[n] * 1e-6) / 1e9, 1) for n in all_gemms},
         "registration_us": {k: round(v, 3) for k, v in registration_us.items()},
         "per_launch_us": per_launch,
         "event_overhead_us": event_overhead,

@@ -280,6 +280,26 @@ int mmq_q6k_limbs_q8t(const void *Wl, int64_t od, int64_t id,
                       void *ws, hipStream_t stream);
 
 /*
+ * mmq_q4k_xf32 -- the q4_K GEMM on fp32 activations, quantized inside the
+ * GEMM (the "quantization fused into the GEMM prologue" direction after the
+ * quantize-transpose prepass, r21 page "Coalesced block-linear A staging",
+ * s5): each workgroup quantizes its 64 tokens of the next super-block
+ * straight into its LDS stage, with the pad40 quantization of
+ * quantize_q8_pad40, so no q8 plane is written or read.  y is bit-identical
+ * to quantize_q8_tiled followed by mmq_q4k_q8t (with the same ws).  Every
+ * row tile of the output quantizes the same tokens again: ceil(od/64) times
+ * the quantization work of the prepass.
+ *   W, od, id, nt, y, ldy, ws as for mmq_q4k_q8t
+ *   x      fp32 activations [nt][ldx], ldx >= id and ldx % 4 == 0, 16-byte
+ *          aligned; read only
+ * Errors: QIG_EINVAL (as mmq_q4k_q8t, or ldx < id), QIG_EALIGN (x, W, y or
+ *         ws misaligned, ldx % 4), QIG_ELAUNCH.
+ */
+int mmq_q4k_xf32(const void *W, int64_t od, int64_t id, const float *x,
+                 int64_t ldx, int64_t nt, float *y, int64_t ldy, void *ws,
+                 hipStream_t stream);
+
+/*
  * mmq_q4k_q8t_noalloc -- mmq_q4k_q8t with a stream-K workspace, for callers
  * that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc).  The call itself

@@ -47,6 +47,7 @@ SIGNATURES = {
     "mmq_q4k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q6k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q4k_q8t_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "mmq_q4k_xf32": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "q6k_limbs_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "prepare_q6k_limbs": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "mmq_q6k_limbs_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
@@ -142,7 +143,7 @@ def _x_rows(x, id_):
     tensor's own (one row: id, which the library accepts as a stride).  The
     last float read must lie inside the tensor's storage."""
     import torch
-    if x.dim() != 2 or x.dtype != torch.float32 or x.stride(1) != 1:
+    if x.dim() != 2 or x.dtype != torch.float32 or (x.numel() > 0 and x.stride(1) != 1):
         raise QigError("x must be a 2-D fp32 tensor with unit column stride")
     nt, width = x.shape
     id_ = width if id_ is None else int(id_)
@@ -385,6 +386,18 @@ def mmq_q4k_q8t(W, od: int, id_: int, q8t, nt: int, y=None, ldy: int | None = No
     _gemm_checks(W, _raw_bytes(od, id_, 144), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q4k_q8t(_dev_ptr(W, "W"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"), ldy,
                               _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_q8t")
+    return y
+
+
+def mmq_q4k_xf32(W, od: int, id_: int, x, y=None, ldy: int | None = None, ws=None, stream=None):
+    """The q4_K GEMM on fp32 activations x[nt][ldx] (GPU), quantized inside
+    the GEMM: y bit-identical to quantize_q8_tiled then mmq_q4k_q8t.  ws:
+    None (whole tiles) or a stream-K workspace."""
+    nt, ldx, id_ = _x_rows(x, id_)
+    y, ldy = _out_y(y, nt, od, ldy, W.device)
+    _gemm_checks(W, _raw_bytes(od, id_, 144), None, 0, nt, od, y, ldy, ws=ws)
+    _check(load().mmq_q4k_xf32(_dev_ptr(W, "W"), od, id_, _dev_ptr(x, "x"), ldx, nt, _dev_ptr(y, "y"), ldy,
+                               _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_xf32")
     return y
 
 

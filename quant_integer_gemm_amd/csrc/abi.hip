@@ -236,6 +236,21 @@ int mmq_q4k_q8t(const void *W, int64_t od, int64_t id, const void *q8t, int64_t 
     return gemm_q4k(W, od, id, q8t, nt, y, ldy, ws, true, stream);
 }
 
+int mmq_q4k_xf32(const void *W, int64_t od, int64_t id, const float *x, int64_t ldx, int64_t nt, float *y,
+                 int64_t ldy, void *ws, hipStream_t stream)
+{
+    if (ldx < id) return QIG_EINVAL;
+    int rc = check_gemm(W, od, id, x, nt, y, ldy, 144);
+    if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    if (ldx % 4 != 0) return QIG_EALIGN;
+    if (ws && !aligned(ws, 16)) return QIG_EALIGN;
+    qig::MmqLaunch L = {4, W, nullptr, x, y, nullptr, 144, od, id, nt, ldy, 0, nt, 0, od};
+    L.ws = ws;
+    L.x_f32 = true;
+    L.ldx = ldx;
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
 int mmq_q6k_q8t(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od, int64_t id, const void *q8t,
                 int64_t nt, float *y, int64_t ldy, void *ws, hipStream_t stream)
 {

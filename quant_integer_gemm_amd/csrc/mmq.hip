@@ -49,6 +49,7 @@
 
 #include "qig_device.h"
 #include "qig_launch.h"
+#include "qig_quant.h"
 
 namespace qig {
 
@@ -73,7 +74,11 @@ constexpr int ARM_LIMB = 3;
 // d and ssum go through registers (d widened, -ssum split into bf16 pairs).
 // TILED: the tiled plane of quantize_q8_tiled, whose records already hold
 // the LDS image of all three, so the whole activation stage is a copy.
-constexpr int ACT_PAD40 = 0, ACT_TILED = 1;
+// F32 (q4_K): the fp32 activations themselves; each workgroup quantizes its
+// 64 tokens of the next super-block into the stage it will compute from
+// (quant_stage), the bytes the tiled record would hold, so no q8 plane goes
+// through memory.
+constexpr int ACT_PAD40 = 0, ACT_TILED = 1, ACT_F32 = 2;
 
 // One super-block of staged operands.
 template <int QT>
@@ -129,7 +134,8 @@ struct Stage<6> {
 struct MmqArgs {
     const uint8_t *W;
     const uint8_t *Wexp;
-    const uint8_t *q8;
+    const uint8_t *q8;        // F32 source: the fp32 activations, ldx floats per token
+    int64_t ldx;
     float *y;
     int32_t *P;
     int64_t bstride, od, id, nt, ldy;
@@ -224,6 +230,10 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
         // copies bytes 16 l .. 16 l + 15 of every 1 KB piece
         s.q8 = g.q8 + (tw0 / 64) * nsb * Q8T_RECORD;
         s.aq[0] = s.aq[1] = 16u * (uint32_t)(tid & 63);
+        s.ad[0] = s.ad[1] = 0;
+    } else if constexpr (ACT == ACT_F32) {
+        s.q8 = nullptr;   // quant_stage reads the activations
+        s.aq[0] = s.aq[1] = 0;
         s.ad[0] = s.ad[1] = 0;
     } else {
         s.q8 = g.q8 + tw0 * (int64_t)tok;
@@ -358,8 +368,33 @@ __device__ __forceinline__ void stage_act(uint32_t sl, const Src &s, int64_t sb,
 {
     if constexpr (ACT == ACT_TILED)
         load_act_tiled<QT>(sl, s, sb, tid);
-    else
+    else if constexpr (ACT == ACT_PAD40)
         load_act<QT>(sl, s, sb, tid);
+    // F32: quant_stage, called where the stage is free to write
+}
+
+// F32 source: quantize super-block sb of the 64 tokens from tw0 into the
+// activation part of stage s (q4_K), the bytes of the tiled record
+// (put_tiled).  Lane group i = tid / 8 takes token i (passes 0-7) and 32 + i
+// (passes 8-15), chunk pass % 8; each lane one float4 of the block.  All 16
+// loads are issued before the first block is quantized.  Tokens past nt are
+// quantized from zeros, as the tiled plane holds them.  The caller makes the
+// stores visible with a barrier before any wave reads the stage.
+__device__ __forceinline__ void quant_stage(const MmqArgs &g, Stage<4> &s, int64_t tw0, int64_t sb, int tid)
+{
+    const int l8 = tid & 7, tg = tid >> 3;
+    float4 v[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const int64_t t = tw0 + tg + 32 * (p >> 3);
+        v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < g.nt)
+            v[p] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(g.q8) + t * g.ldx +
+                                                     256 * sb + 32 * (p & 7) + 4 * l8);
+    }
+    uint8_t *r = reinterpret_cast<uint8_t *>(&s);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) put_tiled(r, p & 7, tg + 32 * (p >> 3), l8, quant_block(v[p]));
 }
 
 // Dense arms: direct global->LDS copies of super-block sb's quants from the
@@ -792,6 +827,7 @@ __device__ __forceinline__ void finish_tile(const MmqArgs &g, const f32x16 &p, c
 template <int QT, int ARM, int MODE, int ACT>
 __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 {
+    static_assert(ACT != ACT_F32 || (QT == 4 && MODE == 0), "the fp32 source is built for the q4_K GEMM");
     __shared__ Stage<QT> st[2];
     const uint32_t sl0 = (uint32_t)(uintptr_t)(lds_void_t *)&st[0];   // LDS address of stage 0
 
@@ -824,6 +860,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
     Src src = make_src<QT, ARM, ACT>(g, tw0, jw0, tid);
     Raw<QT, ARM> rw;
     stage_act<QT, ACT>(sl0, src, cur.k0, tid);
+    if constexpr (ACT == ACT_F32) quant_stage(g, st[0], tw0, cur.k0, tid);
     if constexpr (ARM != ARM_RAW && QT == 6) load_wexp<QT>(sl0, src, cur.k0, tid);
     if constexpr (QT == 4) load_bq<ARM>(sl0, src, cur.k0, tid);
     load_raw<QT, ARM, ACT>(rw, src, cur.k0, tid);
@@ -914,7 +951,10 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
                 }
                 if constexpr (MODE == 0) pin(acc);                  // epilogue c done here
             }
-            if (more) store_raw<QT, ARM, ACT>(sn, rw, tid);
+            if (more) {
+                if constexpr (ACT == ACT_F32) quant_stage(g, sn, tw0, sb + 1, tid);
+                store_raw<QT, ARM, ACT>(sn, rw, tid);
+            }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             ph ^= 1;
@@ -933,6 +973,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
             src = make_src<QT, ARM, ACT>(g, nt0, nj0, tid);
             const uint32_t slp = sl0 + ph * (uint32_t)sizeof(Stage<QT>);
             stage_act<QT, ACT>(slp, src, nxt.k0, tid);
+            if constexpr (ACT == ACT_F32) quant_stage(g, st[ph], nt0, nxt.k0, tid);
             if constexpr (ARM != ARM_RAW && QT == 6) load_wexp<QT>(slp, src, nxt.k0, tid);
             if constexpr (QT == 4) load_bq<ARM>(slp, src, nxt.k0, tid);
             load_raw<QT, ARM, ACT>(rw, src, nxt.k0, tid);
@@ -1080,8 +1121,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_limbs_kernel(MmqArgs g)
         const int nsteps = 2 * (cur.k1 - cur.k0);
         float dnext = 0.0f;
         for (int stp = 0; stp < nsteps; ++stp) {
-            const int64_t sb = cur.k0 + (stp >> 1);
-            const int hs = stp & 1;
+            const int hs = stp & 1;   // half of super-block cur.k0 + stp / 2
             const StageL &s = st[ph];
             const bool more = stp + 1 < nsteps;
             const uint32_t sln = sl0 + (ph ^ 1) * (uint32_t)sizeof(StageL);
@@ -1268,6 +1308,7 @@ int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
     g.W = static_cast<const uint8_t *>(Lc.W);
     g.Wexp = reinterpret_cast<const uint8_t *>(Lc.Wexp);
     g.q8 = static_cast<const uint8_t *>(Lc.q8);
+    g.ldx = Lc.ldx;
     g.y = Lc.y;
     g.P = Lc.P;
     g.bstride = Lc.bstride;
@@ -1290,6 +1331,10 @@ int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
     if (Lc.limbs) {
         if (part || !Lc.q8_tiled || Lc.qtype != 6) return -1;
         return launch<6, ARM_LIMB, 0, ACT_TILED>(g, wsw, clr, stream);
+    }
+    if (Lc.x_f32) {
+        if (part || Lc.qtype != 4 || Lc.prepared || Lc.q8_tiled) return -1;
+        return launch<4, ARM_RAW, 0, ACT_F32>(g, wsw, clr, stream);
     }
     if (Lc.q8_tiled) {
         // whole-output GEMMs only (the partials exports read pad40)

@@ -41,6 +41,8 @@ struct MmqLaunch {
     int64_t ws_workers = 1024;     // workgroups the workspace has partial slots and counters for
     bool clear_counters = false;   // zero the arrival counters before a split launch
     bool limbs = false;      // q6_K limb buffer: W = its d plane, Wexp = its H plane (L plane follows)
+    bool x_f32 = false;      // q8 points to fp32 activations (ldx floats per token), quantized in the GEMM
+    int64_t ldx = 0;
 };
 
 // Stream-K workspace: two 64 x 64 fp32 partial-sum slots per worker, then

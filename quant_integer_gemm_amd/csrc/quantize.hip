@@ -18,95 +18,9 @@
 // the campaign moving to), so the GEMM stages activations by plain copies.
 #include "qig_device.h"
 #include "qig_launch.h"
+#include "qig_quant.h"
 
 namespace qig {
-
-__device__ __forceinline__ float round_half_away(float v)
-{
-    float r = __builtin_truncf(v);
-    if (__builtin_fabsf(v - r) >= 0.5f) r += __builtin_copysignf(1.0f, v);
-    return r;
-}
-
-// Reductions over the 8 lanes of a group (lanes 8g .. 8g+7) with DPP moves:
-// swap neighbours, swap pairs in a quad, then mirror within the half row.
-template <int CTRL>
-__device__ __forceinline__ int dpp(int v)
-{
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ float group8_max(float v)
-{
-    v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(int, v))));
-    v = __builtin_fmaxf(v, __builtin_bit_cast(float, dpp<0x4E>(__builtin_bit_cast(int, v))));
-    return __builtin_fmaxf(v, __builtin_bit_cast(float, dpp<0x141>(__builtin_bit_cast(int, v))));
-}
-__device__ __forceinline__ int group8_sum(int v)
-{
-    v += dpp<0xB1>(v);
-    v += dpp<0x4E>(v);
-    return v + dpp<0x141>(v);
-}
-
-// round-half-away(x / d) for d > 0 from the product with an approximate
-// reciprocal r.  With r within 2 ulps of 1/d, x * r rounded differs from the
-// correctly rounded quotient by less than 1.5 * 2^-22 relative, so by less
-// than 2^-14 for |x / d| <= 128.  Unless x * r lies within 2^-13 of a tie
-// (k + 1/2), both are in the same rounding interval and give the same
-// integer; *near is set otherwise and the caller takes the IEEE quotient.
-__device__ __forceinline__ float round_fast(float x, float r, bool &near)
-{
-    const float qa = x * r;
-    const float t = __builtin_truncf(qa);
-    const float f = __builtin_fabsf(qa - t);
-    near = __builtin_fabsf(f - 0.5f) < 0x1p-13f;
-    return f >= 0.5f ? t + __builtin_copysignf(1.0f, qa) : t;
-}
-
-// One 32-element block, eight lanes each holding four of its values (lane l8
-// holds elements 4*l8 .. 4*l8+3): the lane's four quant bytes, and on every
-// lane the fp16 d bits and ssum.
-struct QBlock {
-    uint32_t packed;   // this lane's four int8 quants
-    uint32_t dbits;    // fp16 d (low half)
-    float ssum;        // d * sum(q), exact
-};
-
-__device__ __forceinline__ QBlock quant_block(float4 v)
-{
-    float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
-                                 __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
-    amax = group8_max(amax);
-    const float d32 = amax / 127.0f;
-    float k[4];
-    const float xs[4] = {v.x, v.y, v.z, v.w};
-    // d32 below 2^-100 (and 0) takes the IEEE path: its reciprocal may not
-    // be finite.
-    const bool tiny = d32 < 0x1p-100f;
-    const float r = __builtin_amdgcn_rcpf(tiny ? 1.0f : d32);
-    bool slow = tiny;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bool nr;
-        k[i] = round_fast(xs[i], r, nr);
-        slow |= nr;
-    }
-    if (slow) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) k[i] = d32 == 0.0f ? 0.0f : round_half_away(xs[i] / d32);
-    }
-    int q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = (int)__builtin_amdgcn_fmed3f(k[i], -127.0f, 127.0f);
-    const int s = group8_sum(q[0] + q[1] + q[2] + q[3]);
-    QBlock o;
-    o.packed = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) | ((uint32_t)(q[2] & 0xff) << 16) |
-               ((uint32_t)(q[3] & 0xff) << 24);
-    const _Float16 dh = (_Float16)d32;
-    o.dbits = (uint32_t)__builtin_bit_cast(uint16_t, dh);
-    o.ssum = (float)dh * (float)s;
-    return o;
-}
 
 __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ x, int64_t nblk,
                                                         int64_t nb32, int64_t ldx,
@@ -177,21 +91,7 @@ __global__ __launch_bounds__(256) void quantize_tiled_kernel(const float *__rest
     }
     uint8_t *r = q8t + (int64_t)rec * Q8T_RECORD;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int tl = tl0 + 32 * u;
-        const QBlock q = quant_block(v[u]);
-        const int h = l8 >> 2;
-        *reinterpret_cast<uint32_t *>(r + 2048 * cc + 32 * tl + 16 * (h ^ swz(tl)) + 4 * (l8 & 3)) = q.packed;
-        if (l8 == 0) {
-            *reinterpret_cast<float *>(r + 16384 + 256 * cc + 4 * x_slot(tl)) = h2f(q.dbits);
-        } else if (l8 == 7) {
-            uint16_t hi, lo;
-            bf16_split(-q.ssum, hi, lo);
-            uint16_t *m = reinterpret_cast<uint16_t *>(r + 18432 + 16 * (2 * tl + (cc >> 2)));
-            m[cc & 3] = hi;
-            m[4 + (cc & 3)] = lo;
-        }
-    }
+    for (int u = 0; u < U; ++u) put_tiled(r, cc, tl0 + 32 * u, l8, quant_block(v[u]));
 }
 
 int launch_quantize(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q8, hipStream_t stream)

@@ -259,3 +259,27 @@ def test_limbs_sizes_and_argument_checks():
     assert lib.mmq_q6k_limbs_q8t(MIS, 8, 256, B16, 4, A16, 8, None, None) == -2
     assert lib.mmq_q6k_limbs_q8t(A16, 8, 256, B16, 4, A16, 8, MIS, None) == -2    # workspace
     assert lib.mmq_q6k_limbs_q8t(A16, 8, 256, B16, 0, A16, 8, None, None) == 0    # nt == 0
+
+
+def test_xf32_argument_checks():
+    lib = qig.load()
+    # (W, od, id, x, ldx, nt, y, ldy, ws, stream)
+    assert lib.mmq_q4k_xf32(A16, 8, 256, B16, 255, 4, A16, 8, None, None) == -1   # ldx < id
+    assert lib.mmq_q4k_xf32(A16, 8, 300, B16, 300, 4, A16, 8, None, None) == -1   # id % 256
+    assert lib.mmq_q4k_xf32(A16, 8, 256, B16, 256, 4, A16, 7, None, None) == -1   # ldy < od
+    assert lib.mmq_q4k_xf32(A16, 8, 256, B16, 258, 4, A16, 8, None, None) == -2   # ldx % 4
+    assert lib.mmq_q4k_xf32(A16, 8, 256, MIS, 256, 4, A16, 8, None, None) == -2   # x
+    assert lib.mmq_q4k_xf32(MIS, 8, 256, B16, 256, 4, A16, 8, None, None) == -2   # W
+    assert lib.mmq_q4k_xf32(A16, 8, 256, B16, 256, 4, A16, 8, MIS, None) == -2    # workspace
+    assert lib.mmq_q4k_xf32(A16, 8, 256, None, 256, 4, A16, 8, None, None) == -1  # no x
+    assert lib.mmq_q4k_xf32(A16, 8, 256, B16, 256, 0, A16, 8, None, None) == 0    # nt == 0
+    assert lib.mmq_q4k_xf32(A16, 0, 256, B16, 256, 4, A16, 8, None, None) == 0    # od == 0
+
+
+def test_xf32_binding_checks_activation_rows():
+    import torch
+    W = torch.zeros(4 * 144, dtype=torch.uint8)
+    with pytest.raises(qig.QigError, match="exceeds"):
+        qig.mmq_q4k_xf32(W, 4, 512, torch.zeros((2, 256), dtype=torch.float32))
+    with pytest.raises(qig.QigError, match="2-D fp32"):
+        qig.mmq_q4k_xf32(W, 4, 256, torch.zeros((2, 256), dtype=torch.float64))
