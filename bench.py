@@ -412,7 +412,7 @@ def run_gemm_set(args):
     ops = {name: 2.0 * nt * od * id_ for (name, qt, od, id_, xin) in spec["gemms"]}
     for n in extra:
         ops[n] = ops[n.split("[")[0]]
-    total_ops = sum(ops.values())
+    total_ops = sum(2.0 * nt * od * id_ for (name, qt, od, id_, xin) in spec["gemms"])   # the step's GEMMs
     gemms = [g[0] for g in spec["gemms"]]
     dom = max(gemms, key=lambda n: per[n])
     achieved = ops[dom] / (per[dom] * 1e-6) / 1e12
