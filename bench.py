@@ -57,11 +57,11 @@ def parse():
     # clocks and measured up to ~10% slow, depending on what ran first
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--workload", choices=["proj", "ffn", "layer", "down", "kv"], default="proj",
+    p.add_argument("--workload", choices=["proj", "ffn", "layer", "layer_q6v", "down", "kv"], default="proj",
                    help="proj: the q4_K and q6_K 3584x3584 nt=512 GEMMs (the headline); ffn: the 7B-class "
                         "FFN GEMMs at nt=512; layer: all seven GEMMs of a 7B-class layer at nt=2630; down: "
                         "the layer's q6_K down projection alone (3584x18944, nt=2630); kv: the layer's k and v "
-                        "projections")
+                        "projections; layer_q6v: the layer with a q6_K v projection")
     p.add_argument("--activations", choices=["tiled", "pad40"], default="tiled",
                    help="ffn / layer workloads: activation plane of the timed step")
     p.add_argument("--copy-calibration", action="store_true",
@@ -303,6 +303,12 @@ GEMM_SETS = {
         ("ffn_gate", "q4_K", 18944, 3584, "x_ffn"), ("ffn_up", "q4_K", 18944, 3584, "x_ffn"),
         ("ffn_down", "q6_K", 3584, 18944, "x_down")]},
     "down": {"nt": 2630, "xscale": 1.0, "gemms": [("ffn_down", "q6_K", 3584, 18944, "x_down")]},
+    # the layer with its v projection stored as q6_K, as the pages' model keeps it in some layers
+    "layer_q6v": {"nt": 2630, "xscale": 1.0, "gemms": [
+        ("attn_q", "q4_K", 3584, 3584, "x_attn"), ("attn_k", "q4_K", 512, 3584, "x_attn"),
+        ("attn_v", "q6_K", 512, 3584, "x_attn"), ("attn_o", "q4_K", 3584, 3584, "x_o"),
+        ("ffn_gate", "q4_K", 18944, 3584, "x_ffn"), ("ffn_up", "q4_K", 18944, 3584, "x_ffn"),
+        ("ffn_down", "q6_K", 3584, 18944, "x_down")]},
     "kv": {"nt": 2630, "xscale": 1.0, "gemms": [
         ("attn_k", "q4_K", 512, 3584, "x_attn"), ("attn_v", "q4_K", 512, 3584, "x_attn")]},
 }
@@ -436,7 +442,9 @@ def run_gemm_set(args):
                          "down": "7B-class layer's q6_K down projection 3584x18944 at nt=2630, after its "
                                  "activation quantization",
                          "kv": "7B-class layer's q4_K k and v projections 512x3584 at nt=2630 after one "
-                               "shared activation quantization"}[args.workload],
+                               "shared activation quantization",
+                         "layer_q6v": "7B-class layer at nt=2630 with a q6_K v projection: q4_K q, k, o, gate, "
+                                      "up and q6_K v and down"}[args.workload],
             "q6k_arm": "limbs" if tiled else "raw",
             "activations": args.activations, "nt": nt,
             "gemms": {g[0]: f"{g[1]} {g[2]}x{g[3]}" for g in spec["gemms"]},

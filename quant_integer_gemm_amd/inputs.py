@@ -103,6 +103,10 @@ WORKLOADS = {
         Gemm("q6K_ffn_down_3584x18944_nt2630", "q6_K", 3584, 18944, 2630)],
 }
 
+# The layer's v projection as q6_K: the pages' model keeps attn_v in q6_K in
+# some layers (r44 page "W_exp stride mismatch root cause", s2.4).
+LAYER_Q6K_ATTN_V = Gemm("q6K_attn_v_512x3584_nt2630", "q6_K", 512, 3584, 2630)
+
 
 def make_gemm_inputs(gm: Gemm, seed: int):
     """(W uint8 2-D, x fp32 [nt, id]) for one GEMM, drawn in recipe order."""

@@ -314,6 +314,13 @@ def _run_workload_gemm(qig, gm, seed):
     assert np.isfinite(yt).all(), f"{gm.name} tiled: non-finite outputs"
     _assert_close(yt, y_ref, gm.name + " tiled plane, stream-K workspace")
     assert int(torch.count_nonzero(ws[-16384:]).item()) == 0
+    if gm.qtype == "q6_K":
+        # the q6_K arm the FFN and layer steps of bench.py run: the limb buffer
+        Wl = qig.prepare_q6k_limbs(Wd, 224, od, id_)
+        yl = host(qig.mmq_q6k_limbs_q8t(Wl, od, id_, q8td, nt, ws=ws))
+        assert np.isfinite(yl).all(), f"{gm.name} limbs: non-finite outputs"
+        _assert_close(yl, y_ref, gm.name + " limb buffer, tiled plane, stream-K workspace")
+        assert int(torch.count_nonzero(ws[-16384:]).item()) == 0
 
 
 # ---------------------------------------------------------------------------
@@ -396,6 +403,12 @@ def test_workload_layer_full(qig, i):
     """The nt=2630 layer: every output of each of its seven GEMMs."""
     gm = inputs.WORKLOADS[4][i]
     _run_workload_gemm(qig, gm, inputs.SEED_BASE + 4 + 10 * i)
+
+
+def test_workload_layer_q6k_attn_v(qig):
+    """The layer's v projection stored as q6_K (as the pages' model keeps it,
+    r44 s2.4): 512 x 3584 at nt = 2630, every output."""
+    _run_workload_gemm(qig, inputs.LAYER_Q6K_ATTN_V, inputs.SEED_BASE + 4 + 10 * 7)
 
 
 # ---------------------------------------------------------------------------
