@@ -72,8 +72,10 @@ def _limbs_y(qig, W, x, od, id_, nt, ws=None, y=None, ldy=None):
     return host(qig.mmq_q6k_limbs_q8t(Wl, od, id_, q8t, nt, ws=ws, y=y, ldy=ldy))
 
 
+# (2000, 1100, 512): 32 x 18 = 576 whole tiles, more than one round of two
+# per CU, so the launch takes the three-per-CU build of the kernel
 SHAPES = [(16, 256, 512), (1, 1, 256), (70, 130, 768), (129, 257, 512), (64, 128, 256), (200, 300, 1024),
-          (3, 1000, 256), (65, 129, 2304), (512, 3584, 3584)]
+          (3, 1000, 256), (65, 129, 2304), (512, 3584, 3584), (2000, 1100, 512)]
 
 
 @pytest.mark.parametrize("nt,od,id_", SHAPES)
