@@ -110,7 +110,7 @@ struct Stage<4> {
     // element 64g + i low and 64g + 32 + i high), its 16-byte unit u at
     // position u ^ ((j / 2) % 8)
     __attribute__((aligned(16))) uint8_t bq[TJ][128];
-    float bs[NCH][TJ];          // d * sc
+    float bs[NCH][TJ][2];       // d * sc, and -M d * sc (the magic term of the epilogue's first fma)
     MinOp mb[TJ][2];            // dmin * m of row j, chunks 4h .. 4h+3
 };
 
@@ -480,8 +480,11 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r, i
             // part p: (d*sc, dmin*m) of sub-blocks 2p and 2p+1; the min-term
             // pair lands in K half p/2, elements 2(p%2), 2(p%2)+1
             uint16_t hi0, lo0, hi1, lo1;
-            s.bs[2 * part][row] = as_float((int)r.h[0]);
-            s.bs[2 * part + 1][row] = as_float((int)r.h[2]);
+            const float w0 = as_float((int)r.h[0]), w1 = as_float((int)r.h[2]);
+            s.bs[2 * part][row][0] = w0;
+            s.bs[2 * part][row][1] = -MAGIC_F * w0;
+            s.bs[2 * part + 1][row][0] = w1;
+            s.bs[2 * part + 1][row][1] = -MAGIC_F * w1;
             bf16_split(as_float((int)r.h[1]), hi0, lo0);
             bf16_split(as_float((int)r.h[3]), hi1, lo1);
             uint32_t *mm = s.mb[row][part >> 1].w;
@@ -502,8 +505,11 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r, i
         const uint32_t s2 = __builtin_amdgcn_ubfe(r.h[3], 8 * part, 8);   // S[part + 8]
         const uint32_t sc0 = s0 & 63, m0 = s1 & 63;
         const uint32_t sc1 = (s2 & 15) | ((s0 >> 2) & 0x30), m1 = (s2 >> 4) | ((s1 >> 2) & 0x30);
-        s.bs[part][row] = d * (float)sc0;
-        s.bs[part + 4][row] = d * (float)sc1;
+        const float w0 = d * (float)sc0, w1 = d * (float)sc1;
+        s.bs[part][row][0] = w0;
+        s.bs[part][row][1] = -MAGIC_F * w0;
+        s.bs[part + 4][row][0] = w1;
+        s.bs[part + 4][row][1] = -MAGIC_F * w1;
         uint16_t hi, lo;
         uint16_t *mm0 = reinterpret_cast<uint16_t *>(&s.mb[row][0]);
         uint16_t *mm1 = reinterpret_cast<uint16_t *>(&s.mb[row][1]);
@@ -557,7 +563,7 @@ struct Ab {                          // MFMA operands of one chunk
 
 template <int QT>
 struct Sc {                          // epilogue scales of one chunk
-    float w0, w1;                    // weight scale (q6_K: of both sub-blocks)
+    float w0, w1;                    // weight scale (q6_K: of both sub-blocks; q4_K: w1 = -M w0)
 };
 
 template <int QT>
@@ -592,7 +598,8 @@ template <int QT>
 __device__ __forceinline__ void load_sc(Sc<QT> &o, const Stage<QT> &s, int c, const Lane &L)
 {
     if constexpr (QT == 4) {
-        o.w0 = s.bs[c][L.jb];
+        o.w0 = s.bs[c][L.jb][0];
+        o.w1 = s.bs[c][L.jb][1];
     } else {
         o.w0 = s.bs[c][L.jb][0];
         o.w1 = s.bs[c][L.jb][1];
@@ -650,8 +657,12 @@ __device__ __forceinline__ void epilogue(const ChunkD<QT> &D, const Sc<QT> &o, c
 {
     if constexpr (MODE == 0) {
         constexpr auto rows = std::make_integer_sequence<int, 16>{};
-        scale_rows(acc, D.v[0], o.w0, -MAGIC_F * o.w0, x, rows);
-        if constexpr (QT == 6) scale_rows(acc, D.v[1], o.w1, -MAGIC_F * o.w1, x, rows);
+        if constexpr (QT == 4) {
+            scale_rows(acc, D.v[0], o.w0, o.w1, x, rows);
+        } else {
+            scale_rows(acc, D.v[0], o.w0, -MAGIC_F * o.w0, x, rows);
+            scale_rows(acc, D.v[1], o.w1, -MAGIC_F * o.w1, x, rows);
+        }
     } else {
         const int64_t nsb = g.id / 256;
         const int64_t nsub = (QT == 4 ? 8 : 16) * nsb;
@@ -1158,6 +1169,14 @@ __global__ __launch_bounds__(NTHR, OCC) void mmq_limbs_kernel(MmqArgs g)
                     xv[c + 2] = s.ax[c + 2][xs];
                 }
                 i32x16 &ch = dh[c & 1], &cl = dl[c & 1];
+                // The epilogue's fmas are inline assembly, and the compiler
+                // inserts no wait states for an inline-asm read of an MFMA
+                // result.  Chunk c's results are read only after chunk c+1's
+                // two MFMAs have issued (the matrix core takes them in order,
+                // so c's are written back by then) or, for the last chunk,
+                // after the whole previous epilogue: far more than the wait
+                // states the hardware needs.  Reading them right after their
+                // own MFMA gives wrong values.
                 if (c + 1 < LCH) {
                     i32x16 &nh = dh[(c + 1) & 1], &nl = dl[(c + 1) & 1];
                     nh = mfma_i8(ah[c + 1], ab[c + 1], bias);
