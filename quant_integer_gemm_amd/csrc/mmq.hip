@@ -1179,12 +1179,13 @@ __global__ __launch_bounds__(NTHR, OCC) void mmq_limbs_kernel(MmqArgs g)
                 i32x16 &ch = dh[c & 1], &cl = dl[c & 1];
                 // The epilogue's fmas are inline assembly, and the compiler
                 // inserts no wait states for an inline-asm read of an MFMA
-                // result.  Chunk c's results are read only after chunk c+1's
-                // two MFMAs have issued (the matrix core takes them in order,
+                // result: read right after its own MFMA, a result is wrong.
+                // Chunk c's results are read only after chunk c+1's MFMAs
+                // have issued (the matrix core runs them one after another,
                 // so c's are written back by then) or, for the last chunk,
-                // after the whole previous epilogue: far more than the wait
-                // states the hardware needs.  Reading them right after their
-                // own MFMA gives wrong values.
+                // after the whole previous epilogue.  A CPU test checks this
+                // order in the built assembly.  (Explicit s_nop padding
+                // instead costs 7-9%.)
                 if (c + 1 < LCH) {
                     i32x16 &nh = dh[(c + 1) & 1], &nl = dl[(c + 1) & 1];
                     nh = mfma_i8(ah[c + 1], ab[c + 1], bias);
