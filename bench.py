@@ -4,13 +4,14 @@
 One step = one pass of the hot path over one batch of synthetic input at the
 q-projection shape (od = id = 3584, nt = 512): one q4_K and one q6_K GEMM,
 each after the quantization of its own activations into the tiled plane:
-    quantize_q8_tiled(x4) -> mmq_q4k_q8t (W4, raw blocks)
+    quantize_q8_tiled(x4) -> mmq_q4k_staged_q8t (W4 as a staged buffer)
     quantize_q8_tiled(x6) -> mmq_q6k_limbs_q8t (W6 as a limb buffer)
 Inputs are resident in HBM before timing.  Registration-time forms of the
-weights (the limb buffer, the dense plane, the prepared buffers) are built
-once beforehand and timed separately.  Every other arm -- q6_K on raw blocks
-and on the dense plane (the two paths the q6_K workload names), the prepared
-buffers, and the pad40 activation plane -- is timed per kernel after the step.
+weights (the staged and limb buffers, the dense plane, the prepared
+buffers) are built once beforehand and timed separately.  Every other arm --
+both types on raw blocks, q6_K on the dense plane (the paths the workloads
+name), the prepared buffers, and the pad40 activation plane -- is timed per
+kernel after the step.
 
 Before the W warmup steps the step runs back to back for --spinup-s seconds
 (untimed), so that a short --warmup does not time a GPU that is still ramping
@@ -312,16 +313,16 @@ GEMM_SETS = {
     "kv": {"nt": 2630, "xscale": 1.0, "gemms": [
         ("attn_k", "q4_K", 512, 3584, "x_attn"), ("attn_v", "q4_K", 512, 3584, "x_attn")]},
 }
-CPU_SAMPLE_TOKENS = 256
 
 
 def run_gemm_set(args):
-    """The FFN, layer or down workload: one quantization per distinct input
-    (tiled plane, or pad40), then its GEMMs, q4_K on raw blocks and q6_K on
-    the limb buffer (tiled plane) or raw blocks (pad40); the stream-K
-    workspace is passed to every GEMM and used where the tile count calls for
-    it.  With the tiled plane each q6_K GEMM is also timed, outside the step,
-    on raw blocks and on the dense plane."""
+    """The FFN, layer, down or k/v workload: one quantization per distinct
+    input (tiled plane, or pad40), then its GEMMs: with the tiled plane q4_K
+    on the staged buffer and q6_K on the limb buffer, with pad40 both on raw
+    blocks; the stream-K workspace is passed to every GEMM and used where the
+    tile count calls for it.  With the tiled plane each GEMM is also timed,
+    outside the step, on raw blocks (q6_K also on the dense plane; q4_K also
+    quantizing its own activations)."""
     import torch
     import quant_integer_gemm_amd as qig
     from quant_integer_gemm_amd import inputs
@@ -330,13 +331,20 @@ def run_gemm_set(args):
     dev = torch.device("cuda:0")
     tiled = args.activations == "tiled"
     ws = qig.new_workspace(dev)
-    xs, qs, Ws, ys, host, limbs, wexps = {}, {}, {}, {}, {}, {}, {}
+    xs, qs, Ws, ys, host, limbs, wexps, staged = {}, {}, {}, {}, {}, {}, {}, {}
     registration_us = {}
     for i, (name, qt, od, id_, xin) in enumerate(spec["gemms"]):
         W, x = inputs.make_gemm_inputs(inputs.Gemm(name, qt, od, id_, nt, spec["xscale"]),
                                        inputs.SEED_BASE + 500 + i)
         Ws[name] = torch.from_numpy(W).to(dev)
         host[name] = W
+        if qt == "q4_K" and tiled:
+            staged[name] = torch.empty(qig.q4k_staged_bytes(od, id_), dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            qig.prepare_q4k_staged(Ws[name], od, id_, out=staged[name])
+            torch.cuda.synchronize()
+            registration_us["prepare_q4k_staged:" + name] = round((time.perf_counter() - t) * 1e6, 1)
         if qt == "q6_K" and tiled:
             limbs[name] = torch.empty(qig.q6k_limbs_bytes(od, id_), dtype=torch.uint8, device=dev)
             wexps[name] = torch.empty((od, id_), dtype=torch.int8, device=dev)
@@ -358,15 +366,18 @@ def run_gemm_set(args):
             return lambda: qig.quantize_q8_tiled(xs[xin], out=qs[xin])
         return lambda: qig.quantize_q8_pad40(xs[xin], out=qs[xin])
 
-    def gemm(name, qt, od, id_, xin, arm="limbs"):
+    def gemm(name, qt, od, id_, xin, arm="registered"):
         W, q8, y = Ws[name], qs[xin], ys[name]
         if qt == "q4_K":
-            if tiled:
+            if tiled and arm == "raw":
                 return lambda: qig.mmq_q4k_q8t(W, od, id_, q8, nt, y=y, ldy=od, ws=ws)
+            if tiled:
+                Wst = staged[name]
+                return lambda: qig.mmq_q4k_staged_q8t(Wst, od, id_, q8, nt, y=y, ldy=od, ws=ws)
             return lambda: qig.mmq_q4k_streamk(W, od, id_, q8, nt, y=y, ldy=od, ws=ws)
         if not tiled:
             return lambda: qig.mmq_q6k_streamk(W, 224, od, id_, q8, nt, y=y, ldy=od, ws=ws)
-        if arm == "limbs":
+        if arm == "registered":
             Wl = limbs[name]
             return lambda: qig.mmq_q6k_limbs_q8t(Wl, od, id_, q8, nt, y=y, ldy=od, ws=ws)
         if arm == "wexp":
@@ -387,6 +398,7 @@ def run_gemm_set(args):
             extra[name + "[raw]"] = gemm(name, qt, od, id_, xin, "raw")
             extra[name + "[wexp]"] = gemm(name, qt, od, id_, xin, "wexp")
         if qt == "q4_K" and tiled:
+            extra[name + "[raw]"] = gemm(name, qt, od, id_, xin, "raw")
             # the same GEMM quantizing its own activations (no q8 plane)
             extra[name + "[xf32]"] = (lambda W=Ws[name], x=xs[xin], y=ys[name], od=od, id_=id_:
                                       qig.mmq_q4k_xf32(W, od, id_, x, y=y, ldy=od, ws=ws))
@@ -445,7 +457,7 @@ def run_gemm_set(args):
                                "shared activation quantization",
                          "layer_q6v": "7B-class layer at nt=2630 with a q6_K v projection: q4_K q, k, o, gate, "
                                       "up and q6_K v and down"}[args.workload],
-            "q6k_arm": "limbs" if tiled else "raw",
+            "weights": "q4_K staged buffer, q6_K limb buffer" if tiled else "raw blocks",
             "activations": args.activations, "nt": nt,
             "gemms": {g[0]: f"{g[1]} {g[2]}x{g[3]}" for g in spec["gemms"]},
         },
@@ -468,27 +480,29 @@ def run_gemm_set(args):
         },
     }
     if not args.no_cpu_baseline:
+        # the whole step on all tokens, once (the layer: about 14 s on 16
+        # cores), with the time of each quantization and GEMM
         import oracle
-        k = min(nt, CPU_SAMPLE_TOKENS)
-        xk = {xin: np.ascontiguousarray(host[xin][:k]) for xin in {g[4] for g in spec["gemms"]}}
-        reps, total = 0, 0.0
-        while total < 10.0 and reps < 100:
-            t0 = time.perf_counter()
-            qh = {}
-            for (name, qt, od, id_, xin) in spec["gemms"]:
-                if xin not in qh:
-                    qh[xin] = oracle.quantize_q8_pad40(xk[xin])
-                if qt == "q4_K":
-                    oracle.mmq_q4k(host[name], od, id_, qh[xin], k)
-                else:
-                    oracle.mmq_q6k(host[name], 224, od, id_, qh[xin], k)
-            total += time.perf_counter() - t0
-            reps += 1
+        parts = {}
+        t_all = time.perf_counter()
+        qh = {}
+        for (name, qt, od, id_, xin) in spec["gemms"]:
+            if xin not in qh:
+                t = time.perf_counter()
+                qh[xin] = oracle.quantize_q8_pad40(host[xin])
+                parts["quantize_" + xin] = time.perf_counter() - t
+            t = time.perf_counter()
+            if qt == "q4_K":
+                oracle.mmq_q4k(host[name], od, id_, qh[xin], nt)
+            else:
+                oracle.mmq_q6k(host[name], 224, od, id_, qh[xin], nt)
+            parts[name] = time.perf_counter() - t
+        total = time.perf_counter() - t_all
         out["cpu_baseline"] = {
-            "value": round(total_ops * k / nt * reps / total / 1e12, 4), "unit": "TOPS",
+            "value": round(total_ops / total / 1e12, 4), "unit": "TOPS",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the first {k} of the {nt} tokens through every quantization and GEMM, "
-                      f"repeated {reps}x in {total:.1f} s",
+            "sample": f"the whole step, all {nt} tokens through every quantization and GEMM, once, in {total:.1f} s",
+            "parts_ms": {k: round(v * 1e3, 1) for k, v in parts.items()},
         }
     print(json.dumps(out), flush=True)
 
@@ -500,7 +514,9 @@ PROFILE_NAMES = {
     "qig::mmq_kernel<6, 2, 0, 0>": "mmq_q6k_prepared", "qig::mmq_kernel<4, 0, 0, 1>": "mmq_q4k_q8t",
     "qig::mmq_kernel<6, 0, 0, 1>": "mmq_q6k_raw_q8t", "qig::mmq_kernel<6, 1, 0, 1>": "mmq_q6k_wexp_q8t",
     "qig::mmq_kernel<4, 2, 0, 1>": "mmq_q4k_prepared_q8t", "qig::mmq_kernel<6, 2, 0, 1>": "mmq_q6k_prepared_q8t",
-    "qig::mmq_limbs_kernel": "mmq_q6k_limbs_q8t", "qig::mmq_kernel<4, 0, 0, 2>": "mmq_q4k_xf32",
+    "qig::mmq_limbs_kernel<2>": "mmq_q6k_limbs_q8t", "qig::mmq_limbs_kernel<3>": "mmq_q6k_limbs_q8t (3 per CU)",
+    "qig::mmq_kernel<4, 0, 0, 2>": "mmq_q4k_xf32", "qig::mmq_kernel<4, 4, 0, 1>": "mmq_q4k_staged_q8t",
+    "qig::prepare_q4k_staged_kernel": "prepare_q4k_staged",
     "qig::prepare_q4k_kernel": "prepare_q4k", "qig::prepare_q6k_scales_kernel": "prepare_q6k (scales)",
     "qig::prepare_q6k_limbs_kernel": "prepare_q6k_limbs",
     "qig::quantize_kernel": "quantize_q8_pad40", "qig::quantize_tiled_kernel<1>": "quantize_q8_tiled",
@@ -535,6 +551,9 @@ def _algorithmic_bytes(nt=NT, od=OD, id_=ID):
         alg[k] = alg[k + "_q8t"] = (w + q8, y)
     alg["mmq_q6k_limbs_q8t"] = (limbs + q8, y)
     alg["mmq_q4k_xf32"] = (raw4 + nt * id_ * 4, y)
+    staged = (od + 63) // 64 * nsb * 14336
+    alg["mmq_q4k_staged_q8t"] = (staged + q8, y)
+    alg["prepare_q4k_staged"] = (raw4, staged)
     alg["quantize_q8_pad40"] = alg["quantize_q8_tiled"] = (nt * id_ * 4, q8)
     alg["expand_q6k_dense"] = (od * nsb * 210, od * id_)
     alg["prepare_q6k_limbs"] = (od * nsb * 210, limbs)
@@ -709,6 +728,7 @@ def main():
     W4p = torch.empty(qig.prepared_bytes("q4_K", OD, ID), dtype=torch.uint8, device=dev)
     W6p = torch.empty(qig.prepared_bytes("q6_K", OD, ID), dtype=torch.uint8, device=dev)
     W6l = torch.empty(qig.q6k_limbs_bytes(OD, ID), dtype=torch.uint8, device=dev)
+    W4s = torch.empty(qig.q4k_staged_bytes(OD, ID), dtype=torch.uint8, device=dev)
 
     # registration-time work, each timed on its own
     def time_us(fn, reps=10):
@@ -727,19 +747,22 @@ def main():
         "prepare_q4k": time_us(lambda: qig.prepare_q4k(W4d, OD, ID, out=W4p)),
         "prepare_q6k": time_us(lambda: qig.prepare_q6k(W6d, 224, OD, ID, out=W6p)),
         "prepare_q6k_limbs": time_us(lambda: qig.prepare_q6k_limbs(W6d, 224, OD, ID, out=W6l)),
+        "prepare_q4k_staged": time_us(lambda: qig.prepare_q4k_staged(W4d, OD, ID, out=W4s)),
     }
 
     # The step: one q4_K and one q6_K GEMM at the q-projection shape, each after
-    # its activation quantization (tiled plane); the q6_K GEMM runs on the limb
-    # buffer, the fastest q6_K arm.  Every other arm and activation form is
-    # timed after it, per kernel.
+    # its activation quantization (tiled plane), each on the fastest
+    # registration-time form of its weights: q4_K on the staged buffer, q6_K on
+    # the limb buffer.  Every other arm (raw blocks among them) and
+    # activation form is timed after it, per kernel.
     steps = {
         "quantize_tiled_x4": lambda: qig.quantize_q8_tiled(x4d, out=t84),
-        "mmq_q4k_q8t": lambda: qig.mmq_q4k_q8t(W4d, OD, ID, t84, NT, y=y4, ldy=OD),
+        "mmq_q4k_staged_q8t": lambda: qig.mmq_q4k_staged_q8t(W4s, OD, ID, t84, NT, y=y4, ldy=OD),
         "quantize_tiled_x6": lambda: qig.quantize_q8_tiled(x6d, out=t86),
         "mmq_q6k_limbs_q8t": lambda: qig.mmq_q6k_limbs_q8t(W6l, OD, ID, t86, NT, y=y6, ldy=OD),
     }
     arms = {
+        "mmq_q4k_q8t": lambda: qig.mmq_q4k_q8t(W4d, OD, ID, t84, NT, y=y4, ldy=OD),
         "mmq_q4k_xf32": lambda: qig.mmq_q4k_xf32(W4d, OD, ID, x4d, y=y4, ldy=OD),
         "mmq_q6k_raw_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, y=y6, ldy=OD),
         "mmq_q6k_wexp_q8t": lambda: qig.mmq_q6k_q8t(W6d, 224, OD, ID, t86, NT, W_exp=wexp, y=y6, ldy=OD),
@@ -812,7 +835,8 @@ def main():
     nsb = ID // 256
     wb = {"mmq_q4k": OD * nsb * 144, "mmq_q6k_raw": OD * nsb * 224, "mmq_q6k_wexp": OD * ID + OD * nsb * 18,
           "mmq_q4k_prepared": qig.prepared_bytes("q4_K", OD, ID), "mmq_q6k_prepared": qig.prepared_bytes("q6_K", OD, ID),
-          "mmq_q6k_limbs": qig.q6k_limbs_bytes(OD, ID), "mmq_q4k_xf32": OD * nsb * 144}
+          "mmq_q6k_limbs": qig.q6k_limbs_bytes(OD, ID), "mmq_q4k_xf32": OD * nsb * 144,
+          "mmq_q4k_staged": qig.q4k_staged_bytes(OD, ID)}
     wbytes = {n: wb[n.replace("_q8t", "")] for n in all_gemms}
     abytes = nb + NT * OD * 4
     # the fused GEMM reads the fp32 activations in place of a q8 plane
@@ -834,8 +858,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "q4_K GEMM and q6_K GEMM, od=id=3584, nt=512, each after its activation quantization "
-                        "(tiled plane); q6_K on the registration-time limb buffer; the raw-block, dense-plane "
-                        "and prepared q6_K arms timed per kernel",
+                        "(tiled plane); q4_K on the registration-time staged buffer, q6_K on the limb buffer; "
+                        "the raw-block, dense-plane and prepared arms timed per kernel",
             "nt": NT, "od": OD, "id": ID, "seeds": [SEED4, SEED6],
         },
         "per_kernel_us": {k: round(v, 3) for k, v in per.items()},

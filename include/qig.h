@@ -280,6 +280,43 @@ int mmq_q6k_limbs_q8t(const void *Wl, int64_t od, int64_t id,
                       void *ws, hipStream_t stream);
 
 /*
+ * Staged q4_K weights -- a registration-time buffer whose records are the
+ * bytes the q4_K GEMM stages into LDS for each 64-row tile and super-block
+ * (the registration-time direction of the pages' prepared planes: r43 page
+ * "PC-sampling attribution + pre-expand-B parity FAIL", s3.2), so that with
+ * the tiled activation plane the GEMM's whole stage is plain copies and no
+ * scale is decoded in the GEMM.  For tile T = j / 64 and super-block sb, a
+ * record of 14336 bytes at ((T * (id/256)) + sb) * 14336 holds, for rows
+ * r = j % 64:
+ *   nibbles  block bytes 16..143 of row r, 16-byte unit u at
+ *            128 r + 16 (u ^ ((r >> 1) & 7))
+ *   scales   for sub-block c (0..7): w = d * sc_c and -1.5 * 2^23 * w,
+ *            fp32, at 8192 + 8 (64 c + r)
+ *   mins     dmin * m of sub-blocks 4h .. 4h+3 (h = 0, 1) split as
+ *            hi = bf16(v) and lo = bf16(v - hi) (round to nearest even):
+ *            16-byte entry at 12288 + 16 (2 r + h), hi at 16-bit index
+ *            c % 4, lo at 4 + c % 4
+ * Rows od .. 64 * ceil(od/64) - 1 are zero.  The layout is part of this
+ * contract.  The buffer takes 1.56 times the raw blocks' memory.
+ *
+ * mmq_q4k_staged_q8t -- y[nt][od] of the q4_K GEMM from a staged buffer and
+ * a tiled activation plane: bit-identical to mmq_q4k_q8t on the same blocks.
+ *   W      raw q4_K blocks as for mmq_q4k (prepare only), 16-byte aligned
+ *   Ws     the staged buffer, q4k_staged_bytes(od, id) bytes, 16-byte
+ *          aligned; prepare writes every byte
+ *   q8t, nt, y, ldy, ws as for mmq_q4k_q8t
+ * q4k_staged_bytes returns 0 for invalid shapes.  prepare_q4k_staged:
+ * QIG_EINVAL (od < 0, id <= 0 or id % 256), QIG_EALIGN, QIG_ELAUNCH.
+ * mmq_q4k_staged_q8t: as mmq_q4k_q8t.
+ */
+size_t q4k_staged_bytes(int64_t od, int64_t id);
+int prepare_q4k_staged(const void *W, int64_t od, int64_t id, void *Ws,
+                       hipStream_t stream);
+int mmq_q4k_staged_q8t(const void *Ws, int64_t od, int64_t id,
+                       const void *q8t, int64_t nt, float *y, int64_t ldy,
+                       void *ws, hipStream_t stream);
+
+/*
  * mmq_q4k_xf32 -- the q4_K GEMM on fp32 activations, quantized inside the
  * GEMM (the "quantization fused into the GEMM prologue" direction after the
  * quantize-transpose prepass, r21 page "Coalesced block-linear A staging",

@@ -48,6 +48,9 @@ SIGNATURES = {
     "mmq_q6k_prepared_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "mmq_q4k_q8t_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]),
     "mmq_q4k_xf32": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "q4k_staged_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "prepare_q4k_staged": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
+    "mmq_q4k_staged_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
     "q6k_limbs_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "prepare_q6k_limbs": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "mmq_q6k_limbs_q8t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
@@ -456,6 +459,34 @@ def mmq_q6k_limbs_q8t(Wl, od: int, id_: int, q8t, nt: int, y=None, ldy: int | No
     _gemm_checks(Wl, q6k_limbs_bytes(od, id_), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
     _check(load().mmq_q6k_limbs_q8t(_dev_ptr(Wl, "Wl"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"), ldy,
                                     _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q6k_limbs_q8t")
+    return y
+
+
+def q4k_staged_bytes(od: int, id_: int) -> int:
+    """Size of a staged q4_K buffer: ceil(od/64) * (id/256) records of 14336 bytes."""
+    return int(load().q4k_staged_bytes(od, id_))
+
+
+def prepare_q4k_staged(W, od: int, id_: int, out=None, stream=None):
+    """Raw q4_K plane -> staged buffer (per 64-row tile and super-block, the
+    bytes the GEMM stages into LDS)."""
+    import torch
+    if out is None:
+        out = torch.empty(q4k_staged_bytes(od, id_), dtype=torch.uint8, device=W.device)
+    _need(W, _raw_bytes(od, id_, 144), "W")
+    _need(out, q4k_staged_bytes(od, id_), "out")
+    _check(load().prepare_q4k_staged(_dev_ptr(W, "W"), od, id_, _dev_ptr(out, "Ws"), _stream(stream)),
+           "prepare_q4k_staged")
+    return out
+
+
+def mmq_q4k_staged_q8t(Ws, od: int, id_: int, q8t, nt: int, y=None, ldy: int | None = None, ws=None, stream=None):
+    """y[nt][od] of the q4_K GEMM from a staged buffer and a tiled activation
+    plane (bit-identical to mmq_q4k_q8t)."""
+    y, ldy = _out_y(y, nt, od, ldy, Ws.device)
+    _gemm_checks(Ws, q4k_staged_bytes(od, id_), q8t, q8_tiled_bytes(nt, id_), nt, od, y, ldy, ws=ws)
+    _check(load().mmq_q4k_staged_q8t(_dev_ptr(Ws, "Ws"), od, id_, _dev_ptr(q8t, "q8t"), nt, _dev_ptr(y, "y"), ldy,
+                                     _dev_ptr(ws, "ws"), _stream(stream)), "mmq_q4k_staged_q8t")
     return y
 
 

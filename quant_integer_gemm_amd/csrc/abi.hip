@@ -257,6 +257,37 @@ int mmq_q6k_q8t(const void *W, int64_t bstride, const int8_t *W_exp, int64_t od,
     return gemm_q6k(W, bstride, W_exp, od, id, q8t, nt, y, ldy, ws, true, stream);
 }
 
+size_t q4k_staged_bytes(int64_t od, int64_t id)
+{
+    if (od < 0 || id <= 0 || id % 256 != 0) return 0;
+    return (size_t)((od + 63) / 64) * (size_t)(id / 256) * (size_t)qig::Q4S_RECORD;
+}
+
+int prepare_q4k_staged(const void *W, int64_t od, int64_t id, void *Ws, hipStream_t stream)
+{
+    if (od < 0 || id <= 0 || id % 256 != 0) return QIG_EINVAL;
+    if (od == 0) return QIG_OK;
+    if (!W || !Ws) return QIG_EINVAL;
+    if (!aligned(W, 16) || !aligned(Ws, 16)) return QIG_EALIGN;
+    return rc_from_launch(qig::launch_prepare_q4k_staged(W, od, id, Ws, stream));
+}
+
+int mmq_q4k_staged_q8t(const void *Ws, int64_t od, int64_t id, const void *q8t, int64_t nt, float *y, int64_t ldy,
+                       void *ws, hipStream_t stream)
+{
+    // a record spans 64 rows of id/256 super-blocks: its byte offsets stay
+    // below 2^31 when the raw blocks' do
+    int rc = check_gemm(Ws, od, id, q8t, nt, y, ldy, 144);
+    if (rc != QIG_OK || nt == 0 || od == 0) return rc;
+    if (ws && !aligned(ws, 16)) return QIG_EALIGN;
+    qig::MmqLaunch L = {4, nullptr, static_cast<const int8_t *>(Ws), q8t, y, nullptr, 144, od, id, nt, ldy,
+                        0, nt, 0, od};
+    L.ws = ws;
+    L.q8_tiled = true;
+    L.staged = true;
+    return rc_from_launch(qig::launch_mmq(L, stream));
+}
+
 size_t q6k_limbs_bytes(int64_t od, int64_t id)
 {
     if (od < 0 || id <= 0 || id % 256 != 0) return 0;

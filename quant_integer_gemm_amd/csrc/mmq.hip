@@ -69,6 +69,10 @@ constexpr int ARM_RAW = 0, ARM_WEXP = 1, ARM_PREP = 2;
 // LIMB (q6_K, tiled activations only): a limb buffer (prepare_q6k_limbs) run
 // by mmq_limbs_kernel, below.
 constexpr int ARM_LIMB = 3;
+// STAGED (q4_K, tiled activations only): a staged buffer (prepare_q4k_staged)
+// whose records are the byte image of the weight part of the stage, so the
+// whole stage -- activations and weights -- arrives by plain copies.
+constexpr int ARM_STAGED = 4;
 
 // Activation sources.  PAD40: the pad40 plane; quants are copied into LDS,
 // d and ssum go through registers (d widened, -ssum split into bf16 pairs).
@@ -117,6 +121,9 @@ struct Stage<4> {
 static_assert(offsetof(Stage<4>, ax) == 16384 && offsetof(Stage<4>, ma) == 18432 &&
                   offsetof(Stage<4>, bq) == Q8T_RECORD,
               "the tiled activation record is the byte image of the first Q8T_RECORD bytes of Stage<4>");
+static_assert(offsetof(Stage<4>, bs) == Q8T_RECORD + 8192 && offsetof(Stage<4>, mb) == Q8T_RECORD + 12288 &&
+                  sizeof(Stage<4>) == Q8T_RECORD + Q4S_RECORD,
+              "a staged q4_K record is the byte image of the last Q4S_RECORD bytes of Stage<4>");
 
 // q6_K: row TT of every chunk plane of a is all zero.  Each 16-element
 // sub-block has its own MFMA, which must see zeros in the lanes that carry
@@ -262,7 +269,12 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
     // weight rows in place of tokens (a row's chunk is 32 plain bytes).
     // q4_K PREP: nibble plane, id/2 bytes per row, 128 per super-block
     s.x = ARM == ARM_RAW ? nullptr : g.Wexp + jw0 * (QT == 4 ? g.id / 2 : g.id);
-    if constexpr (QT == 4) {
+    if constexpr (ARM == ARM_STAGED) {
+        // the row tile's records (tiles start at multiples of 64 rows); lane l
+        // copies bytes 16 l .. 16 l + 15 of every 1 KB piece
+        s.x = g.Wexp + (jw0 / 64) * nsb * Q4S_RECORD;
+        s.xq[0] = s.xq[1] = 16u * (uint32_t)(tid & 63);
+    } else if constexpr (QT == 4) {
         // packed nibble copies: wave w's copy i fills rows 16w + 8i .. +7 of
         // Stage::bq; lane l writes position l % 8 of row 16w + 8i + l / 8,
         // which holds unit (l % 8) ^ ((row / 2) % 8) of the row's 128 bytes
@@ -417,6 +429,16 @@ template <int ARM>
 __device__ __forceinline__ void load_bq(uint32_t sl, const Src &s, int64_t sb, int tid)
 {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    if constexpr (ARM == ARM_STAGED) {
+        // the record's 14 pieces of 1 KB: wave w copies pieces w, w+4, w+8, w+12
+        const uint8_t *rec = s.x + sb * Q4S_RECORD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = w + 4 * i;
+            if (p < Q4S_RECORD / 1024) dma16(rec + 1024 * p, s.xq[0], sl + offsetof(Stage<4>, bq) + 1024 * p);
+        }
+        return;
+    }
     const uint8_t *base = ARM == ARM_PREP ? s.x + sb * 128 : s.w + sb * 144;
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(base, s.xq[i], sl + offsetof(Stage<4>, bq) + (16 * w + 8 * i) * 128);
@@ -435,6 +457,7 @@ __device__ __forceinline__ void load_raw(Raw<QT, ARM> &r, const Src &s, int64_t 
             r.as[1] = *reinterpret_cast<const uint32_t *>(q8 + 36 + s.ad[1]);
         }
     }
+    if constexpr (ARM == ARM_STAGED) return;   // the weight stage is all copies (load_bq)
     const uint8_t *blk = s.w + sb * s.wstep + s.wo;
     if constexpr (ARM == ARM_PREP) {
         r.h = ld16(blk + 16 * part);
@@ -474,7 +497,9 @@ __device__ __forceinline__ void store_raw(Stage<QT> &s, const Raw<QT, ARM> &r, i
             m[4 + (c & 3)] = lo;
         }
     }
-    if constexpr (ARM == ARM_PREP) {
+    if constexpr (ARM == ARM_STAGED) {
+        // the weight stage came with the copies
+    } else if constexpr (ARM == ARM_PREP) {
         // this lane's 16 bytes of the row's scale block
         if constexpr (QT == 4) {
             // part p: (d*sc, dmin*m) of sub-blocks 2p and 2p+1; the min-term
@@ -839,6 +864,8 @@ template <int QT, int ARM, int MODE, int ACT>
 __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 {
     static_assert(ACT != ACT_F32 || (QT == 4 && MODE == 0), "the fp32 source is built for the q4_K GEMM");
+    static_assert(ARM != ARM_STAGED || (QT == 4 && MODE == 0 && ACT == ACT_TILED),
+                  "the staged buffer is built for the q4_K GEMM on the tiled plane");
     __shared__ Stage<QT> st[2];
     const uint32_t sl0 = (uint32_t)(uintptr_t)(lds_void_t *)&st[0];   // LDS address of stage 0
 
@@ -1370,6 +1397,11 @@ int launch_mmq(const MmqLaunch &Lc, hipStream_t stream)
     if (Lc.x_f32) {
         if (part || Lc.qtype != 4 || Lc.prepared || Lc.q8_tiled) return -1;
         return launch<4, ARM_RAW, 0, ACT_F32>(g, wsw, clr, stream);
+    }
+    if (Lc.staged) {
+        // records are per 64-row tile: the output window must start at row 0
+        if (part || Lc.qtype != 4 || !Lc.q8_tiled || Lc.j0 != 0) return -1;
+        return launch<4, ARM_STAGED, 0, ACT_TILED>(g, wsw, clr, stream);
     }
     if (Lc.q8_tiled) {
         // whole-output GEMMs only (the partials exports read pad40)

@@ -122,6 +122,75 @@ int launch_prepare_q6k_limbs(const void *W, int64_t bstride, int64_t od, int64_t
                          reinterpret_cast<float *>(H + 2 * od * id));
 }
 
+// q4_K staged buffer: per 64-row tile T and super-block sb a record of
+// Q4S_RECORD bytes at (T * nsb + sb) * Q4S_RECORD, the byte image of the
+// weight part of the GEMM's LDS stage:
+//   [0, 8192)      the packed nibble bytes (block bytes 16..143) of rows
+//                  r = 0..63 of the tile: 16-byte unit u of row r at
+//                  128 r + 16 (u ^ ((r >> 1) & 7))
+//   [8192, 12288)  for chunk (sub-block) c and row r, at 8192 + 8 (64 c + r):
+//                  w = d * sc_c and -M w (fp32; M = 1.5 * 2^23, the
+//                  epilogue's magic bias)
+//   [12288, 14336) for row r and K half h, at 12288 + 16 (2 r + h): dmin *
+//                  m of chunks 4h .. 4h+3 split as bf16 hi (16-bit indices
+//                  0-3) and lo = bf16(v - hi) (indices 4-7)
+// Rows past od are zero.  One workgroup per record: thread (r, p) = (tid %
+// 64, tid / 64) writes nibble units 2p, 2p+1 and the scales of sub-blocks
+// p and p + 4 of row r, with the raw-block GEMM's arithmetic, so y is
+// bit-identical to mmq_q4k_q8t.
+__global__ __launch_bounds__(256) void prepare_q4k_staged_kernel(const uint8_t *__restrict__ W, int64_t od,
+                                                                  int64_t id, uint8_t *__restrict__ R)
+{
+    const int64_t nsb = id / 256;
+    const int64_t rec = blockIdx.x;
+    const int64_t T = rec / nsb, sb = rec - T * nsb;
+    const int r = threadIdx.x & 63, p = threadIdx.x >> 6;
+    const int64_t j = 64 * T + r;
+    uint8_t *out = R + rec * Q4S_RECORD;
+    u32x4 q[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+    float w[2] = {0.0f, 0.0f}, mm[2] = {0.0f, 0.0f};
+    if (j < od) {
+        const uint8_t *blk = W + (j * nsb + sb) * 144;
+        const u32x4 hdr = *reinterpret_cast<const u32x4 *>(blk);
+        q[0] = *reinterpret_cast<const u32x4 *>(blk + 16 + 32 * p);
+        q[1] = *reinterpret_cast<const u32x4 *>(blk + 32 + 32 * p);
+        uint8_t sbytes[12];
+#pragma unroll
+        for (int k = 0; k < 12; ++k) sbytes[k] = (uint8_t)(hdr[1 + (k >> 2)] >> (8 * (k & 3)));
+        const float d = h2f(hdr[0]), dmin = h2f(hdr[0] >> 16);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            int sc, m;
+            q4_scale_min(sbytes, p + 4 * k, sc, m);
+            w[k] = d * (float)sc;
+            mm[k] = dmin * (float)m;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int u = 2 * p + k;
+        *reinterpret_cast<u32x4 *>(out + 128 * r + 16 * (u ^ ((r >> 1) & 7))) = q[k];
+        const int c = p + 4 * k;
+        float *ws = reinterpret_cast<float *>(out + 8192 + 8 * (64 * c + r));
+        ws[0] = w[k];
+        ws[1] = j < od ? -MAGIC_F * w[k] : 0.0f;   // +0 in the zero rows past od
+        uint16_t hi, lo;
+        bf16_split(mm[k], hi, lo);
+        uint16_t *mb = reinterpret_cast<uint16_t *>(out + 12288 + 16 * (2 * r + k));
+        mb[p] = hi;
+        mb[4 + p] = lo;
+    }
+}
+
+int launch_prepare_q4k_staged(const void *W, int64_t od, int64_t id, void *R, hipStream_t stream)
+{
+    const int64_t nrec = (od + 63) / 64 * (id / 256);
+    if (nrec == 0) return 0;
+    if (nrec > 0x7fffffff) return -1;
+    return launch_kernel(prepare_q4k_staged_kernel, dim3((unsigned)nrec), dim3(256), stream,
+                         static_cast<const uint8_t *>(W), od, id, static_cast<uint8_t *>(R));
+}
+
 int launch_prepare_q4k(const void *W, int64_t od, int64_t id, int8_t *Q, float *S, hipStream_t stream)
 {
     const int64_t n = od * (id / 256) * 4;

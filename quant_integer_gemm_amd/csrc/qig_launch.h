@@ -43,6 +43,7 @@ struct MmqLaunch {
     bool limbs = false;      // q6_K limb buffer: W = its d plane, Wexp = its H plane (L plane follows)
     bool x_f32 = false;      // q8 points to fp32 activations (ldx floats per token), quantized in the GEMM
     int64_t ldx = 0;
+    bool staged = false;     // q4_K staged buffer: Wexp = its records (W unused)
 };
 
 // Stream-K workspace: two 64 x 64 fp32 partial-sum slots per worker, then
@@ -76,6 +77,9 @@ int launch_expand_q6k(const void *W, int64_t bstride, int64_t od, int64_t id, in
 // register order, bf16 hi/lo pairs of -ssum [64][2][8] -- the first bytes of
 // the GEMM's LDS stage, so the GEMM copies it without conversion.
 constexpr int64_t Q8T_RECORD = 20480;
+// Staged q4_K weights: one record of Q4S_RECORD bytes per (64-row tile,
+// super-block), the byte image of the weight part of the GEMM's LDS stage.
+constexpr int64_t Q4S_RECORD = 14336;
 int launch_quantize_tiled(const float *x, int64_t nt, int64_t id, int64_t ldx, void *q8t, hipStream_t stream);
 // Prepared buffers: quant plane (q6_K: [od][id] centred int8; q4_K:
 // [od][id/2] packed nibble bytes), then scale plane [od][id/256][16] fp32
@@ -84,6 +88,7 @@ int launch_quantize_tiled(const float *x, int64_t nt, int64_t id, int64_t ldx, v
 int launch_prepare_q4k(const void *W, int64_t od, int64_t id, int8_t *Q, float *S, hipStream_t stream);
 // q6_K limb buffer: H plane int8 [od][id], L plane int8 [od][id], then d
 // plane fp32 [od][id/256]; v = sc * c6 = 128 H + L per element.
+int launch_prepare_q4k_staged(const void *W, int64_t od, int64_t id, void *R, hipStream_t stream);
 int launch_prepare_q6k_limbs(const void *W, int64_t bstride, int64_t od, int64_t id, void *Wl, hipStream_t stream);
 int launch_prepare_q6k_scales(const void *W, int64_t bstride, int64_t od, int64_t id, float *S,
                               hipStream_t stream);

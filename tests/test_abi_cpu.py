@@ -283,3 +283,19 @@ def test_xf32_binding_checks_activation_rows():
         qig.mmq_q4k_xf32(W, 4, 512, torch.zeros((2, 256), dtype=torch.float32))
     with pytest.raises(qig.QigError, match="2-D fp32"):
         qig.mmq_q4k_xf32(W, 4, 256, torch.zeros((2, 256), dtype=torch.float64))
+
+
+def test_staged_sizes_and_argument_checks():
+    lib = qig.load()
+    assert qig.q4k_staged_bytes(3584, 3584) == 56 * 14 * 14336
+    assert qig.q4k_staged_bytes(65, 256) == 2 * 14336
+    assert qig.q4k_staged_bytes(4, 100) == 0 and qig.q4k_staged_bytes(-1, 256) == 0
+    assert lib.prepare_q4k_staged(A16, 4, 100, B16, None) == -1        # id % 256
+    assert lib.prepare_q4k_staged(MIS, 4, 256, B16, None) == -2
+    assert lib.prepare_q4k_staged(A16, 4, 256, MIS, None) == -2
+    assert lib.prepare_q4k_staged(A16, 0, 256, B16, None) == 0         # od == 0
+    assert lib.mmq_q4k_staged_q8t(A16, 8, 300, B16, 4, A16, 8, None, None) == -1   # id % 256
+    assert lib.mmq_q4k_staged_q8t(A16, 8, 256, B16, 4, A16, 7, None, None) == -1   # ldy < od
+    assert lib.mmq_q4k_staged_q8t(MIS, 8, 256, B16, 4, A16, 8, None, None) == -2
+    assert lib.mmq_q4k_staged_q8t(A16, 8, 256, B16, 4, A16, 8, MIS, None) == -2    # workspace
+    assert lib.mmq_q4k_staged_q8t(A16, 8, 256, B16, 0, A16, 8, None, None) == 0    # nt == 0

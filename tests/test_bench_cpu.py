@@ -48,7 +48,7 @@ def test_summarize_profiles_proj(tmp_path):
     src = tmp_path / "prof"
     out = tmp_path / "out"
     out.mkdir()
-    limb = "qig::mmq_limbs_kernel"
+    limb = "qig::mmq_limbs_kernel<2>"
     q4 = "qig::mmq_kernel<4, 0, 0, 1>"
     _write_csv(str(src / "trace" / "t_kernel_trace.csv"),
                [_trace_row(limb, 1000 * i, 30 + i, 3136) for i in range(5)]

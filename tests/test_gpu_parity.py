@@ -314,6 +314,12 @@ def _run_workload_gemm(qig, gm, seed):
     assert np.isfinite(yt).all(), f"{gm.name} tiled: non-finite outputs"
     _assert_close(yt, y_ref, gm.name + " tiled plane, stream-K workspace")
     assert int(torch.count_nonzero(ws[-16384:]).item()) == 0
+    if gm.qtype == "q4_K":
+        # the q4_K arm the FFN and layer steps of bench.py run: the staged buffer
+        Wst = qig.prepare_q4k_staged(Wd, od, id_)
+        ys = host(qig.mmq_q4k_staged_q8t(Wst, od, id_, q8td, nt, ws=ws))
+        assert np.array_equal(ys.view(np.uint32), yt.view(np.uint32)), f"{gm.name}: staged differs from raw"
+        assert int(torch.count_nonzero(ws[-16384:]).item()) == 0
     if gm.qtype == "q6_K":
         # the q6_K arm the FFN and layer steps of bench.py run: the limb buffer
         Wl = qig.prepare_q6k_limbs(Wd, 224, od, id_)
