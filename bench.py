@@ -99,10 +99,12 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(kernel: str):
-    """HBM bytes per launch of `kernel`, from the counter summary kept under
-    profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when
-    there is none or the kernel source changed since it was taken."""
+def recorded_counter(kernel: str, field: str = "bytes_per_launch"):
+    """A per-launch figure of `kernel` from the counter summary kept under
+    profiles/: HBM bytes (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy) or
+    VALU instructions (SQ_INSTS_VALU - SQ_INSTS_MFMA, wave instructions), or
+    None when there is none or the kernel source changed since it was
+    taken."""
     path = os.path.join(ROOT, "profiles", "mmq_traffic.json")
     try:
         with open(path) as f:
@@ -111,8 +113,35 @@ def recorded_traffic(kernel: str):
         return None
     if rec.get("kernel_code_sha256") != kernel_source_digest():
         return None
-    v = rec.get("bytes_per_launch", {}).get(kernel)
+    v = rec.get(field, {}).get(kernel)
     return None if v is None else int(v)
+
+
+def recorded_traffic(kernel: str):
+    return recorded_counter(kernel, "bytes_per_launch")
+
+
+# Unpacked fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes per
+# clock at 2.4 GHz (the published 157.3 TFLOP/s counts packed fp32, two
+# fused multiply-adds per lane per clock; the kernels are built without
+# packed fp32).  In lane operations per second, 10^12.
+PEAK_VALU_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def valu_roofline(kernel, us, clock_mhz):
+    """The kernel against the VALU issue rate, the bound of its epilogue:
+    VALU wave instructions per launch (recorded counters) x 64 lanes over its
+    average duration, against PEAK_VALU_TLANEOPS (and that peak at the
+    measured clock).  None without recorded counters for the current code."""
+    n = recorded_counter(kernel, "valu_insts_per_launch")
+    if n is None:
+        return None
+    achieved = n * 64 / (us * 1e-6) / 1e12
+    out = {"insts_per_launch": n, "achieved": round(achieved, 2), "peak": PEAK_VALU_TLANEOPS,
+           "unit": "T lane-op/s", "frac": round(achieved / PEAK_VALU_TLANEOPS, 4)}
+    if clock_mhz:
+        out["frac_at_clock"] = round(achieved / (PEAK_VALU_TLANEOPS * clock_mhz / 2400.0), 4)
+    return out
 
 
 def smi_clock_mhz():
@@ -682,9 +711,15 @@ def summarize_profiles(src_dir, workload="proj", out_dir=None):
         f.write("\n".join(lines) + "\n")
     if workload != "proj":
         return
+    valu = {}
+    for k, n in PROFILE_NAMES.items():
+        c = cnt.get(k)
+        if n.startswith("mmq") and c and "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c:
+            valu[n] = int(round(c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]))
     rec = {"kernel_code_sha256": kernel_source_digest(), "fetch_scale": round(fs, 5), "write_scale": round(wsc, 5),
            "source": f"profiles/{tag}_counters.md",
-           "bytes_per_launch": {k: v for k, v in traffic.items() if k.startswith("mmq")}}
+           "bytes_per_launch": {k: v for k, v in traffic.items() if k.startswith("mmq")},
+           "valu_insts_per_launch": valu}
     with open(os.path.join(out_dir, "mmq_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
 
@@ -886,6 +921,7 @@ def main():
             "hbm_achieved_gbs": round(dom_bytes / (per[dom] * 1e-6) / 1e9, 1),
             "hbm_peak_gbs": PEAK_HBM_GBS,
             "hbm_frac": round(dom_bytes / (per[dom] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "valu": valu_roofline(dom, per[dom], clock_mhz),
         },
         "roofline_frac_per_arm": {n: round(gemm_ops / (per[n] * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)
                                   for n in all_gemms},
