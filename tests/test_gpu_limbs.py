@@ -138,7 +138,10 @@ def test_limbs_integer_special_case_exact(qig):
     assert np.array_equal(y.astype(np.float64), want)
 
 
-@pytest.mark.parametrize("nt,od,id_", [(64, 64, 10240), (100, 200, 2048), (33, 700, 4096), (2630, 512, 3584)])
+# (2000, 1100, 512): 576 tiles, more than two per CU but at most 3/4 of three
+# per CU, so the split runs on the three-per-CU build over all its slots
+@pytest.mark.parametrize("nt,od,id_", [(64, 64, 10240), (100, 200, 2048), (33, 700, 4096), (2630, 512, 3584),
+                                       (2000, 1100, 512)])
 def test_limbs_streamk_matches_oracle(qig, nt, od, id_):
     """Tiles split between workgroups (stream-K workspace): within tolerance,
     counters back to zero, and y bit-identical from call to call."""
