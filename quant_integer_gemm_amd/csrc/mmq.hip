@@ -118,7 +118,7 @@ struct Stage<4> {
     MinOp mb[TJ][2];            // dmin * m of row j, chunks 4h .. 4h+3
 };
 
-static_assert(offsetof(Stage<4>, ax) == 16384 && offsetof(Stage<4>, ma) == 18432 &&
+static_assert(offsetof(Stage<4>, a) == 0 && offsetof(Stage<4>, ax) == 16384 && offsetof(Stage<4>, ma) == 18432 &&
                   offsetof(Stage<4>, bq) == Q8T_RECORD,
               "the tiled activation record is the byte image of the first Q8T_RECORD bytes of Stage<4>");
 static_assert(offsetof(Stage<4>, bs) == Q8T_RECORD + 8192 && offsetof(Stage<4>, mb) == Q8T_RECORD + 12288 &&
@@ -301,19 +301,26 @@ __device__ __forceinline__ Src make_src(const MmqArgs &g, int64_t tw0, int64_t j
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Direct global->LDS copy of 16 bytes per lane: lane l's bytes at
-// base + voff land at LDS byte address lds + 16 l (base and lds wave-
-// uniform).  It is issued from inline assembly because the compiler, unable
-// to tell the copy's LDS bytes from those the compute reads, otherwise waits
-// for every outstanding global load at the first such read, which kept each
-// step's loads from overlapping its compute.  The compiler therefore does
-// not know about these copies: their data is read only after an explicit
-// vmcnt(0) wait and a barrier, and since loads complete in order, extra
-// untracked loads only make the compiler's own counted waits stricter.  M0
-// (the LDS address register) is read when the copy issues and is restored
-// afterwards.
-__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32_t lds)
+// Direct global->LDS copies of 16 bytes per lane.  dma16n<N> copies N
+// consecutive 1 KB pieces: lane l's bytes at base + voff + 1024 i land at LDS
+// byte address lds + 1024 i + 16 l (base and lds wave-uniform).  The
+// instruction's offset field moves the global and the LDS address alike (a
+// probe on the device confirmed it), so a run of pieces laid out the same in
+// memory and in the stage needs one M0 (the LDS address register) and one
+// base for up to four pieces.  The copies are issued from inline assembly
+// because the compiler, unable to tell the copy's LDS bytes from those the
+// compute reads, otherwise waits for every outstanding global load at the
+// first such read, which kept each step's loads from overlapping its compute.
+// The compiler therefore does not know about these copies: their data is
+// read only after an explicit vmcnt(0) wait and a barrier, and since loads
+// complete in order, extra untracked loads only make the compiler's own
+// counted waits stricter.  M0 is an input operand, so the compiler writes it
+// and knows its value; the leading s_nop is the wait state an LDS copy needs
+// after an M0 write.
+template <int N>
+__device__ __forceinline__ void dma16n(const uint8_t *base, uint32_t voff, uint32_t lds)
 {
+    static_assert(N >= 1 && N <= 4, "the offset field reaches 4095 bytes: at most four 1 KB pieces");
     // base and lds are wave-uniform; readfirstlane puts them in scalar
     // registers, as the instruction requires, whatever the compiler infers.
     // (readfirstlane returns a signed int: each half goes through uint32_t
@@ -323,15 +330,41 @@ __device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
     const uint64_t sbase = (uint64_t)lo | ((uint64_t)hi << 32);
     const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
-    uint32_t keep;
-    asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %3\n\t"
-                 "s_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, %2\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(keep)
-                 : "v"(voff), "s"(sbase), "s"(m0v)
-                 : "memory");
+    if constexpr (N == 1)
+        asm volatile("s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %0, %1"
+                     :
+                     : "v"(voff), "s"(sbase), "{m0}"(m0v)
+                     : "memory");
+    else if constexpr (N == 2)
+        asm volatile("s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:1024"
+                     :
+                     : "v"(voff), "s"(sbase), "{m0}"(m0v)
+                     : "memory");
+    else if constexpr (N == 3)
+        asm volatile("s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:2048"
+                     :
+                     : "v"(voff), "s"(sbase), "{m0}"(m0v)
+                     : "memory");
+    else
+        asm volatile("s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %0, %1\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+                     "global_load_lds_dwordx4 %0, %1 offset:3072"
+                     :
+                     : "v"(voff), "s"(sbase), "{m0}"(m0v)
+                     : "memory");
+}
+
+__device__ __forceinline__ void dma16(const uint8_t *base, uint32_t voff, uint32_t lds)
+{
+    dma16n<1>(base, voff, lds);
 }
 
 // LDS byte addresses: the copies take the stage's address (sl, computed
@@ -358,21 +391,24 @@ __device__ __forceinline__ void load_act(uint32_t sl, const Src &s, int64_t sb, 
 // Tiled activations: the record of super-block sb holds the first
 // Q8T_RECORD bytes of the q4_K stage (quants, d table, min-term operands)
 // byte for byte; q6_K takes the quants, into its chunk planes (which keep a
-// zero row after each), and the d table.  Pieces of 1 KB: wave w copies
-// quant pieces w, w + 4, w + 8, w + 12 (chunk p / 2, token half p % 2), then
-// piece 16 + w of the scale tables (q6_K: d only, waves 0 and 1).
+// zero row after each), and the d table.  Pieces of 1 KB.  q4_K: wave w
+// copies the record's pieces 5w .. 5w + 4, which land at the same offsets in
+// the stage.  q6_K: wave w copies chunks 2w and 2w + 1 (two pieces each),
+// waves 0 and 1 also piece 16 + w (the d table).
 template <int QT>
 __device__ __forceinline__ void load_act_tiled(uint32_t sl, const Src &s, int64_t sb, int tid)
 {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const uint8_t *rec = s.q8 + sb * Q8T_RECORD;
+    if constexpr (QT == 4) {
+        dma16n<4>(rec + 5120 * w, s.aq[0], sl + 5120 * w);
+        dma16n<1>(rec + 5120 * w + 4096, s.aq[0], sl + 5120 * w + 4096);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = w + 4 * i;
-        dma16(rec + 1024 * p, s.aq[0],
-              sl + offsetof(Stage<QT>, a) + (2 * i + (w >> 1)) * A_PLANE<QT> + 1024 * (w & 1));
+        for (int k = 0; k < 2; ++k)
+            dma16n<2>(rec + 2048 * (2 * w + k), s.aq[0], sl + offsetof(Stage<QT>, a) + (2 * w + k) * A_PLANE<QT>);
+        if (w < 2) dma16(rec + 1024 * (16 + w), s.aq[0], sl + offsetof(Stage<QT>, ax) + 1024 * w);
     }
-    if (QT == 4 || w < 2) dma16(rec + 1024 * (16 + w), s.aq[0], sl + offsetof(Stage<QT>, ax) + 1024 * w);
 }
 
 template <int QT, int ACT>
@@ -430,13 +466,16 @@ __device__ __forceinline__ void load_bq(uint32_t sl, const Src &s, int64_t sb, i
 {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     if constexpr (ARM == ARM_STAGED) {
-        // the record's 14 pieces of 1 KB: wave w copies pieces w, w+4, w+8, w+12
+        // the record's 14 pieces of 1 KB, which land at the same offsets in
+        // the stage: waves 0 and 1 copy pieces 4w .. 4w + 3, waves 2 and 3
+        // pieces 8 + 3 (w - 2) .. + 2
+        static_assert(Q4S_RECORD == 14 * 1024, "the staged record is 14 pieces");
         const uint8_t *rec = s.x + sb * Q4S_RECORD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = w + 4 * i;
-            if (p < Q4S_RECORD / 1024) dma16(rec + 1024 * p, s.xq[0], sl + offsetof(Stage<4>, bq) + 1024 * p);
-        }
+        const uint32_t lb = sl + offsetof(Stage<4>, bq);
+        if (w < 2)
+            dma16n<4>(rec + 4096 * w, s.xq[0], lb + 4096 * w);
+        else
+            dma16n<3>(rec + 8192 + 3072 * (w - 2), s.xq[0], lb + 8192 + 3072 * (w - 2));
         return;
     }
     const uint8_t *base = ARM == ARM_PREP ? s.x + sb * 128 : s.w + sb * 144;
@@ -1099,8 +1138,7 @@ __device__ __forceinline__ void issue_l(uint32_t sl, const SrcL &s, const MmqArg
     const uint8_t *rec = s.q8 + sb * Q8T_RECORD;
     const uint8_t *hb = s.hl + 256 * sb + 32 * c;
     if constexpr (P == 0) {
-        dma16(rec + 2048 * c, lo, sl + offsetof(StageL, a) + 2048 * w);
-        dma16(rec + 2048 * c + 1024, lo, sl + offsetof(StageL, a) + 2048 * w + 1024);
+        dma16n<2>(rec + 2048 * c, lo, sl + offsetof(StageL, a) + 2048 * w);
         dma16(hb, s.xq[0], sl + offsetof(StageL, h) + 2048 * w);
         if (w == 0) dma16(rec + 16384 + 1024 * hs, lo, sl + offsetof(StageL, ax));
     } else {
