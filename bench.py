@@ -121,24 +121,30 @@ def recorded_traffic(kernel: str):
     return recorded_counter(kernel, "bytes_per_launch")
 
 
-# Unpacked fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes per
-# clock at 2.4 GHz (the published 157.3 TFLOP/s counts packed fp32, two
-# fused multiply-adds per lane per clock; the kernels are built without
-# packed fp32).  In lane operations per second, 10^12.
-PEAK_VALU_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# fp32 VALU rate of MI355X: 256 CUs x 4 SIMDs x 32 lanes per clock at
+# 2.4 GHz, in lane operations (one fma per lane) per second, 10^12: the
+# published 157.3 TFLOP/s.  Probe kernels on the device reach it with the
+# unpacked VOP3 v_fma_f32 (about 2 cycles per wave instruction per SIMD) once
+# 4 waves share a SIMD.  A wave issues at most one instruction per 4 cycles,
+# so at 2 waves per SIMD, the occupancy of these kernels, independent fmas
+# reach 2.7 cycles per wave instruction: VALU_CEIL_2W of the peak.
+PEAK_VALU_TLANEOPS = 256 * 4 * 32 * 2.4e9 / 1e12
+VALU_CEIL_2W = 0.74
 
 
 def valu_roofline(kernel, us, clock_mhz):
-    """The kernel against the VALU issue rate, the bound of its epilogue:
-    VALU wave instructions per launch (recorded counters) x 64 lanes over its
-    average duration, against PEAK_VALU_TLANEOPS (and that peak at the
-    measured clock).  None without recorded counters for the current code."""
+    """The kernel against the VALU rate, the bound of its epilogue: VALU wave
+    instructions per launch (recorded counters) x 64 lanes over its average
+    duration, against PEAK_VALU_TLANEOPS, against the ceiling at 2 waves per
+    SIMD, and against the peak at the measured clock.  None without recorded
+    counters for the current code."""
     n = recorded_counter(kernel, "valu_insts_per_launch")
     if n is None:
         return None
     achieved = n * 64 / (us * 1e-6) / 1e12
     out = {"insts_per_launch": n, "achieved": round(achieved, 2), "peak": PEAK_VALU_TLANEOPS,
-           "unit": "T lane-op/s", "frac": round(achieved / PEAK_VALU_TLANEOPS, 4)}
+           "unit": "T lane-op/s", "frac": round(achieved / PEAK_VALU_TLANEOPS, 4),
+           "frac_of_2wave_ceiling": round(achieved / (VALU_CEIL_2W * PEAK_VALU_TLANEOPS), 4)}
     if clock_mhz:
         out["frac_at_clock"] = round(achieved / (PEAK_VALU_TLANEOPS * clock_mhz / 2400.0), 4)
     return out
