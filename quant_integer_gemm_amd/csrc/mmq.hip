@@ -315,8 +315,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // read only after an explicit vmcnt(0) wait and a barrier, and since loads
 // complete in order, extra untracked loads only make the compiler's own
 // counted waits stricter.  M0 is an input operand, so the compiler writes it
-// and knows its value; the leading s_nop is the wait state an LDS copy needs
-// after an M0 write.
+// and knows its value.  The compiler inserts no wait states before inline
+// assembly, so the copy brings its own: a VMEM instruction must follow a VALU
+// write of an SGPR it reads by 5 wait states (the scalar base often comes
+// from v_readfirstlane_b32 right before; read early, the copy takes the
+// register's previous value as its address), and an LDS copy must follow an
+// M0 write by 1.  The leading s_nop 4 gives 5.
 template <int N>
 __device__ __forceinline__ void dma16n(const uint8_t *base, uint32_t voff, uint32_t lds)
 {
@@ -331,20 +335,20 @@ __device__ __forceinline__ void dma16n(const uint8_t *base, uint32_t voff, uint3
     const uint64_t sbase = (uint64_t)lo | ((uint64_t)hi << 32);
     const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
     if constexpr (N == 1)
-        asm volatile("s_nop 0\n\t"
+        asm volatile("s_nop 4\n\t"
                      "global_load_lds_dwordx4 %0, %1"
                      :
                      : "v"(voff), "s"(sbase), "{m0}"(m0v)
                      : "memory");
     else if constexpr (N == 2)
-        asm volatile("s_nop 0\n\t"
+        asm volatile("s_nop 4\n\t"
                      "global_load_lds_dwordx4 %0, %1\n\t"
                      "global_load_lds_dwordx4 %0, %1 offset:1024"
                      :
                      : "v"(voff), "s"(sbase), "{m0}"(m0v)
                      : "memory");
     else if constexpr (N == 3)
-        asm volatile("s_nop 0\n\t"
+        asm volatile("s_nop 4\n\t"
                      "global_load_lds_dwordx4 %0, %1\n\t"
                      "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
                      "global_load_lds_dwordx4 %0, %1 offset:2048"
@@ -352,7 +356,7 @@ __device__ __forceinline__ void dma16n(const uint8_t *base, uint32_t voff, uint3
                      : "v"(voff), "s"(sbase), "{m0}"(m0v)
                      : "memory");
     else
-        asm volatile("s_nop 0\n\t"
+        asm volatile("s_nop 4\n\t"
                      "global_load_lds_dwordx4 %0, %1\n\t"
                      "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
                      "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
