@@ -10,6 +10,7 @@ exact on the integer special case.
 import numpy as np
 import pytest
 
+import layouts
 import oracle
 from quant_integer_gemm_amd import inputs
 
@@ -35,22 +36,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-def _expected_planes(W, bstride, od, id_):
-    """H, L (int8 [od][id]) and d (fp32 [od][nsb]) from the oracle's decoder."""
-    nsb = id_ // 256
-    Wb = W.reshape(od, nsb, bstride)
-    v = np.zeros((od, id_), dtype=np.int32)
-    d = np.zeros((od, nsb), dtype=np.float32)
-    for j in range(od):
-        for sb in range(nsb):
-            c6, sc, dd = oracle.q6k_decode_block(Wb[j, sb])
-            v[j, 256 * sb:256 * sb + 256] = sc.astype(np.int32).repeat(16) * c6.astype(np.int32)
-            d[j, sb] = dd
-    H = v >> 7
-    L = v & 127
-    assert np.array_equal(128 * H + L, v)
-    assert H.min() >= -32 and H.max() <= 32 and L.min() >= 0 and L.max() <= 127
-    return H.astype(np.int8), L.astype(np.int8), d
+_expected_planes = layouts.limb_planes
 
 
 @pytest.mark.parametrize("od,id_,bstride", [(130, 768, 224), (64, 256, 240), (17, 512, 224)])

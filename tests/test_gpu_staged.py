@@ -9,6 +9,7 @@ tiles and stream-K) and within the output tolerance of the oracle."""
 import numpy as np
 import pytest
 
+import layouts
 import oracle
 from quant_integer_gemm_amd import inputs
 
@@ -37,44 +38,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-def _bf16_rne(v):
-    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
-
-
-def _expected_records(W, od, id_):
-    nsb = id_ // 256
-    ntile = (od + 63) // 64
-    out = np.zeros((ntile, nsb, REC), dtype=np.uint8)
-    Wb = W.reshape(od, nsb, 144)
-    for j in range(od):
-        T, r = divmod(j, 64)
-        for sb in range(nsb):
-            blk = Wb[j, sb]
-            q, sc, m, d, dmin = oracle.q4k_decode_block(blk)
-            # the packed bytes decode to the oracle's quants (low nibble of
-            # byte 32g + i: element 64g + i; high: element 64g + 32 + i)
-            nib = blk[16:144]
-            g, i = np.divmod(np.arange(128), 32)
-            assert np.array_equal(nib & 15, q[64 * g + i]) and np.array_equal(nib >> 4, q[64 * g + 32 + i])
-            rec = out[T, sb]
-            for u in range(8):
-                pos = 128 * r + 16 * (u ^ ((r >> 1) & 7))
-                rec[pos:pos + 16] = nib[16 * u:16 * u + 16]
-            w = np.float32(d) * sc.astype(np.float32)            # d is an fp16 value: exact in fp32
-            mm = np.float32(dmin) * m.astype(np.float32)
-            for c in range(8):
-                pair = np.array([w[c], -MAGIC * w[c]], dtype=np.float32)
-                rec[8192 + 8 * (64 * c + r):8192 + 8 * (64 * c + r) + 8] = pair.view(np.uint8)
-            for h in range(2):
-                v = mm[4 * h:4 * h + 4]
-                hi = _bf16_rne(v)
-                lo = _bf16_rne(v - (hi << 16).astype(np.uint32).view(np.float32))
-                ent = np.zeros(8, dtype=np.uint16)
-                ent[:4] = hi
-                ent[4:] = lo
-                rec[12288 + 16 * (2 * r + h):12288 + 16 * (2 * r + h) + 16] = ent.view(np.uint8)
-    return out.reshape(-1)
+_expected_records = layouts.staged_records
 
 
 @pytest.mark.parametrize("od,id_", [(130, 512), (64, 256), (1, 768)])

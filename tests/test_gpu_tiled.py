@@ -10,6 +10,7 @@ and within the output tolerance of the oracle on small shapes.
 import numpy as np
 import pytest
 
+import layouts
 import oracle
 import xkinds
 from quant_integer_gemm_amd import inputs
@@ -38,45 +39,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-def _bf16_rne(v):
-    """float32 array -> bf16 bits (round to nearest even), as uint32 in the low half."""
-    u = v.astype(np.float32).view(np.uint32).astype(np.uint64)
-    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
-
-
-def _tiled_expected(q8, nt, id_):
-    """The tiled plane from a pad40 plane, per the layout the header states."""
-    nb32, nsb, ntt = id_ // 32, id_ // 256, (nt + 63) // 64
-    blk = np.zeros((ntt * 64, nb32, 40), dtype=np.uint8)
-    blk[:nt] = q8.reshape(nt, nb32, 40)                  # padding tokens: quantized zeros
-    d = blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float32)
-    qs = blk[:, :, 4:36]
-    ssum = blk[:, :, 36:40].copy().view(np.float32)[:, :, 0]
-    out = np.zeros((ntt, nsb, REC), dtype=np.uint8)
-    u = np.arange(64)
-    s = ((u >> 2) ^ (u >> 3)) & 1
-    slot = (u & 32) + 16 * ((u >> 2) & 1) + 4 * ((u & 31) >> 3) + (u & 3)
-    for T in range(ntt):
-        tok = slice(64 * T, 64 * T + 64)
-        for sb in range(nsb):
-            rec = out[T, sb]
-            for c in range(8):
-                ch = 8 * sb + c
-                rows = qs[tok, ch]                                    # [64][32]
-                for h in range(2):
-                    base = 2048 * c + 32 * u + 16 * (h ^ s)
-                    idx = base[:, None] + np.arange(16)[None, :]
-                    rec[idx] = rows[:, 16 * h:16 * h + 16]
-                dv = np.zeros(64, dtype=np.float32)
-                dv[slot] = d[tok, ch]
-                rec[16384 + 256 * c:16384 + 256 * c + 256] = dv.view(np.uint8)
-                v = (-ssum[tok, ch]).astype(np.float32)
-                hi = _bf16_rne(v)
-                lo = _bf16_rne(v - (hi << 16).astype(np.uint32).view(np.float32))
-                m = rec[18432:20480].view(np.uint16).reshape(64, 2, 8)
-                m[:, c // 4, c % 4] = hi.astype(np.uint16)
-                m[:, c // 4, 4 + c % 4] = lo.astype(np.uint16)
-    return out.reshape(-1)
+_tiled_expected = layouts.tiled_plane
 
 
 @pytest.mark.parametrize("nt,id_,kind", [(16, 512, "normal"), (70, 768, "zeros"), (1, 256, "normal"),
