@@ -1086,7 +1086,7 @@ __global__ __launch_bounds__(NTHR, 2) void mmq_kernel(MmqArgs g)
 // its rows, tokens its columns), so the activation scale of a chunk is one
 // value per lane rather than sixteen per lane from LDS.  Per chunk and output:
 //   t = fma(D_H, 128, -129 M) = 128 P_H - M          (D = M + P, M = 1.5 2^23;
-//   u = fma(D_L, 1, t)         = 128 P_H + P_L = Q    both exact: |Q| < 2^24)
+//   u = D_L + t                = 128 P_H + P_L = Q    both exact: |Q| < 2^24)
 //   acc = fma(u, da, acc)                            (rounded once)
 // and per super-block y = fma(acc, d, y).  Steps are half super-blocks (four
 // chunks): the limbs double the weight bytes, and a full super-block stage
@@ -1269,7 +1269,7 @@ __global__ __launch_bounds__(NTHR, OCC) void mmq_limbs_kernel(MmqArgs g)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     float u;
-                    asm("v_fma_f32 %0, %1, 1.0, %2" : "=v"(u) : "v"(as_float(cl[i])), "v"(t[i]));
+                    asm("v_add_f32 %0, %1, %2" : "=v"(u) : "v"(as_float(cl[i])), "v"(t[i]));
                     t[i] = u;
                 }
                 pin(t);
