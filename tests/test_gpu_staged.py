@@ -17,8 +17,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-REC = 14336
-MAGIC = np.float32(12582912.0)
+REC = layouts.Q4S_RECORD
 
 
 @pytest.fixture(scope="module")

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-REC = 20480
+REC = layouts.Q8T_RECORD
 
 
 @pytest.fixture(scope="module")
