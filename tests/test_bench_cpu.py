@@ -86,6 +86,38 @@ def test_summarize_profiles_layer_trace_only(tmp_path):
     assert not (out / "mmq_layer_nt2630_counters.md").exists()
 
 
+def test_valu_roofline(monkeypatch):
+    """insts x 64 lanes / duration against 256 CUs x 4 SIMDs x 32 lanes x
+    2.4 GHz, and against 0.74 of that (the two-wave ceiling); None without
+    recorded counters."""
+    monkeypatch.setattr(bench, "recorded_counter", lambda k, f="bytes_per_launch": 10_000_000)
+    r = bench.valu_roofline("mmq_q6k_limbs_q8t", 32.0, 2000)
+    achieved = 10_000_000 * 64 / 32e-6 / 1e12
+    peak = 256 * 4 * 32 * 2.4e9 / 1e12
+    assert r["peak"] == pytest.approx(78.6432)
+    assert r["achieved"] == pytest.approx(achieved, abs=0.01)
+    assert r["frac"] == pytest.approx(achieved / peak, abs=1e-4)
+    assert r["frac_of_2wave_ceiling"] == pytest.approx(achieved / (0.74 * peak), abs=1e-4)
+    assert r["frac_at_clock"] == pytest.approx(achieved / (peak * 2000 / 2400), abs=1e-4)
+    monkeypatch.setattr(bench, "recorded_counter", lambda k, f="bytes_per_launch": None)
+    assert bench.valu_roofline("mmq_q6k_limbs_q8t", 32.0, 2000) is None
+
+
+def test_recorded_counter_guard(tmp_path, monkeypatch):
+    """A recorded figure is returned only while the kernel sources hash to
+    the digest it was taken on."""
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"kernel_code_sha256": bench.kernel_source_digest(), "valu_insts_per_launch": {"k": 7}}
+    (prof / "mmq_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: rec["kernel_code_sha256"])
+    assert bench.recorded_counter("k", "valu_insts_per_launch") == 7
+    assert bench.recorded_counter("other", "valu_insts_per_launch") is None
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
+    assert bench.recorded_counter("k", "valu_insts_per_launch") is None
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
