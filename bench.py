@@ -736,7 +736,7 @@ def main():
         summarize_profiles(args.summarize_profiles, args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is described, not built).", file=sys.stderr)
         sys.exit(2)
 
